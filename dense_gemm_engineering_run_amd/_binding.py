@@ -1,0 +1,160 @@
+"""ctypes binding of libmi355_gemm.so -- argument marshalling only.
+
+Every function here forwards to the C ABI of the same name (see
+include/mi355_gemm.h); all GEMM work runs in the library's HIP kernels.  There
+is no fallback: importing this module fails loudly when the library has not
+been built.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmi355_gemm.so")
+DEFAULT_TABLE = os.path.join(HERE, "tuning", "table.txt")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m dense_gemm_engineering_run_amd.build, or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _int, _chr, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_char, ctypes.c_void_p
+_RUN_ARGS = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.gemm_run.argtypes = _RUN_ARGS
+_lib.gemm_run.restype = _int
+_lib.gemm_run_config.argtypes = _RUN_ARGS + [_int]
+_lib.gemm_run_config.restype = _int
+_lib.gemm_status_str.argtypes = [_int]
+_lib.gemm_status_str.restype = ctypes.c_char_p
+_lib.gemm_num_configs.argtypes = [_int]
+_lib.gemm_num_configs.restype = _int
+_lib.gemm_config_describe.argtypes = [_int, _int, ctypes.c_char_p, ctypes.c_size_t]
+_lib.gemm_config_describe.restype = _int
+_lib.gemm_select_config.argtypes = [_i64, _i64, _i64, _chr, _chr, _chr, _int]
+_lib.gemm_select_config.restype = _int
+_lib.gemm_last_config.argtypes = []
+_lib.gemm_last_config.restype = _int
+_lib.gemm_load_tuning.argtypes = [ctypes.c_char_p]
+_lib.gemm_load_tuning.restype = _int
+_lib.gemm_tuning_size.argtypes = []
+_lib.gemm_tuning_size.restype = _int
+
+# gemm_dtype_t
+DTYPE_F32, DTYPE_F16_F32, DTYPE_BF16_BF16, DTYPE_F16_F16, DTYPE_BF16_F32 = range(5)
+DTYPE_NAMES = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"]
+
+# gemm_status_t
+(GEMM_OK, GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR, GEMM_ERR_BAD_DTYPE, GEMM_ERR_BAD_LD,
+ GEMM_ERR_NULL_PTR, GEMM_ERR_MISALIGNED, GEMM_ERR_ALIAS, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP,
+ GEMM_ERR_TUNING_FILE) = range(11)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"gemm status {status}: {gemm_status_str(status)}")
+
+
+def _c(ch):
+    return ch.encode() if isinstance(ch, str) else bytes([ch])
+
+
+def gemm_run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream=0):
+    """C ABI gemm_run; A, B, C and stream are integer addresses. Returns the status."""
+    return _lib.gemm_run(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                         lda, ldb, ldc, stream)
+
+
+def gemm_run_config(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,
+                    config_id):
+    return _lib.gemm_run_config(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                                lda, ldb, ldc, stream, config_id)
+
+
+def gemm_status_str(status):
+    return _lib.gemm_status_str(status).decode()
+
+
+def gemm_num_configs(dtype):
+    return _lib.gemm_num_configs(dtype)
+
+
+def gemm_config_describe(dtype, config_id):
+    buf = ctypes.create_string_buffer(128)
+    st = _lib.gemm_config_describe(dtype, config_id, buf, len(buf))
+    if st != GEMM_OK:
+        raise GemmError(st)
+    return buf.value.decode()
+
+
+def gemm_select_config(M, N, K, a_major, b_major, c_major, dtype):
+    return _lib.gemm_select_config(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype)
+
+
+def gemm_last_config():
+    return _lib.gemm_last_config()
+
+
+def gemm_load_tuning(path):
+    return _lib.gemm_load_tuning(None if path is None else os.fsencode(path))
+
+
+def gemm_tuning_size():
+    return _lib.gemm_tuning_size()
+
+
+# ---------------------------------------------------------------- torch convenience
+
+def _major(t, first, second):
+    """Major character of a 2-D tensor view: `first` if dim 0 is contiguous."""
+    s0, s1 = t.stride()
+    if s1 == 1 and (s0 >= max(1, t.shape[1]) or t.shape[0] <= 1):
+        return second, s0 if t.shape[0] > 1 else max(1, t.shape[1])
+    if s0 == 1 and (s1 >= max(1, t.shape[0]) or t.shape[1] <= 1):
+        return first, s1 if t.shape[1] > 1 else max(1, t.shape[0])
+    raise ValueError(f"tensor with strides {t.stride()} has no contiguous dimension")
+
+
+def dtype_code(in_dtype, out_dtype):
+    import torch
+    table = {(torch.float32, torch.float32): DTYPE_F32,
+             (torch.float16, torch.float32): DTYPE_F16_F32,
+             (torch.bfloat16, torch.bfloat16): DTYPE_BF16_BF16,
+             (torch.float16, torch.float16): DTYPE_F16_F16,
+             (torch.bfloat16, torch.float32): DTYPE_BF16_F32}
+    try:
+        return table[(in_dtype, out_dtype)]
+    except KeyError:
+        raise ValueError(f"unsupported dtype pair {in_dtype} -> {out_dtype}") from None
+
+
+def gemm(a, b, c, stream=None, config=None):
+    """C = A * B^T for torch device tensors: a is (M, K), b is (N, K), c is (M, N),
+    each a 2-D view with one contiguous dimension.  Majors and leading dims are
+    read from the strides; the stream defaults to torch's current stream."""
+    import torch
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(c.shape) != (M, N):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    am, lda = _major(a, "m", "k")
+    bm, ldb = _major(b, "n", "k")
+    cm, ldc = _major(c, "m", "n")
+    code = dtype_code(a.dtype, c.dtype)
+    if b.dtype != a.dtype:
+        raise ValueError("a and b must have the same dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(c.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args = (M, N, K, am, bm, cm, code, a.data_ptr(), b.data_ptr(), c.data_ptr(), lda, ldb, ldc,
+            stream)
+    st = gemm_run(*args) if config is None else gemm_run_config(*args, config)
+    if st != GEMM_OK:
+        raise GemmError(st)
+    return c
+
+
+if not os.environ.get("MI355_GEMM_TUNING") and os.path.exists(DEFAULT_TABLE):
+    gemm_load_tuning(DEFAULT_TABLE)

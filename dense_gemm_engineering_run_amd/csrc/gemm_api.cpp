@@ -1,0 +1,400 @@
+// gemm_api.cpp -- host side of the C ABI declared in include/mi355_gemm.h.
+//
+// Argument checks (all before any HIP call), the C-m-major swap, tile config
+// selection from the tuning table, and the launch.  The interface follows the
+// pages' problem statement: device pointers, M/N/K, per-operand majors and
+// leading dimensions, and a stream (CuTe DSL Ampere SGEMM example: docstring,
+// SGemm.__call__ and run(); CK Tile practice GEMM README, "Kernel Launch").
+#include "mi355_gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "gemm_kernel.hpp"
+
+namespace {
+
+struct DtypeInfo {
+    const char* name;
+    int in_bytes, out_bytes;
+    const mg::KernelEntry* (*entries)(int*);
+};
+
+const DtypeInfo kDtypes[GEMM_NUM_DTYPES] = {
+    {"f32", 4, 4, mg::entries_f32},
+    {"f16_f32", 2, 4, mg::entries_f16_f32},
+    {"bf16_bf16", 2, 2, mg::entries_bf16_bf16},
+    {"f16_f16", 2, 2, mg::entries_f16_f16},
+    {"bf16_f32", 2, 4, mg::entries_bf16_f32},
+};
+
+const mg::KernelEntry* entries(int dtype, int* n)
+{
+    if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) { *n = 0; return nullptr; }
+    return kDtypes[dtype].entries(n);
+}
+
+int find_config(int dtype, const std::string& name)
+{
+    int n = 0;
+    const mg::KernelEntry* e = entries(dtype, &n);
+    for (int i = 0; i < n; ++i)
+        if (name == e[i].name) return i;
+    return -1;
+}
+
+// ---------------------------------------------------------------- arguments
+
+struct Canon {
+    int64_t M, N, K;
+    char a, b;            // 'k'/'m' and 'k'/'n' after the swap
+    const void* A;
+    const void* B;
+    int64_t lda, ldb, ldc;
+    uint64_t a_bytes, b_bytes;
+};
+
+// Bytes spanned by `outer` rows of `ld` elements whose last row holds
+// `inner` elements rounded up to 16 bytes.
+uint64_t padded_extent(int64_t outer, int64_t inner, int64_t ld, int es)
+{
+    if (outer <= 0 || inner <= 0) return 0;
+    uint64_t last = ((uint64_t)inner * es + 15) / 16 * 16;
+    return (uint64_t)(outer - 1) * (uint64_t)ld * es + last;
+}
+
+uint64_t written_extent(int64_t outer, int64_t inner, int64_t ld, int es)
+{
+    if (outer <= 0 || inner <= 0) return 0;
+    return ((uint64_t)(outer - 1) * (uint64_t)ld + (uint64_t)inner) * es;
+}
+
+bool overlap(const void* p, uint64_t pn, const void* q, uint64_t qn)
+{
+    if (!p || !q || pn == 0 || qn == 0) return false;
+    uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + qn && b < a + pn;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char& c_major,
+             int dtype, const void* A, const void* B, const void* C, int64_t lda, int64_t ldb,
+             int64_t ldc)
+{
+    const int64_t kMaxDim = (int64_t)1 << 30;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_BAD_SHAPE;
+    a_major = (char)std::tolower((unsigned char)a_major);
+    b_major = (char)std::tolower((unsigned char)b_major);
+    c_major = (char)std::tolower((unsigned char)c_major);
+    if ((a_major != 'k' && a_major != 'm') || (b_major != 'k' && b_major != 'n') ||
+        (c_major != 'n' && c_major != 'm'))
+        return GEMM_ERR_BAD_MAJOR;
+    if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return GEMM_ERR_BAD_DTYPE;
+    const int es = kDtypes[dtype].in_bytes, eo = kDtypes[dtype].out_bytes;
+
+    const int64_t a_inner = a_major == 'k' ? K : M, a_outer = a_major == 'k' ? M : K;
+    const int64_t b_inner = b_major == 'k' ? K : N, b_outer = b_major == 'k' ? N : K;
+    const int64_t c_inner = c_major == 'n' ? N : M, c_outer = c_major == 'n' ? M : N;
+    if (lda < std::max<int64_t>(1, a_inner) || ldb < std::max<int64_t>(1, b_inner) ||
+        ldc < std::max<int64_t>(1, c_inner))
+        return GEMM_ERR_BAD_LD;
+
+    const bool reads = M > 0 && N > 0 && K > 0;
+    const bool writes = M > 0 && N > 0;
+    if ((reads && (!A || !B)) || (writes && !C)) return GEMM_ERR_NULL_PTR;
+
+    if (reads && (((uintptr_t)A | (uintptr_t)B) & 15)) return GEMM_ERR_MISALIGNED;
+    if (writes && ((uintptr_t)C & 15)) return GEMM_ERR_MISALIGNED;
+    if ((lda * es) % 16 || (ldb * es) % 16 || (ldc * eo) % 16) return GEMM_ERR_MISALIGNED;
+
+    if (writes) {
+        uint64_t cn = written_extent(c_outer, c_inner, ldc, eo);
+        if (reads && (overlap(C, cn, A, padded_extent(a_outer, a_inner, lda, es)) ||
+                      overlap(C, cn, B, padded_extent(b_outer, b_inner, ldb, es))))
+            return GEMM_ERR_ALIAS;
+    }
+    return GEMM_OK;
+}
+
+// C m-major: C^T (N x M, n-major) = B * A^T.  Swap the operands and sizes.
+Canon canonicalise(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype,
+                   const void* A, const void* B, int64_t lda, int64_t ldb, int64_t ldc)
+{
+    Canon x;
+    if (c == 'm') {
+        x.M = N; x.N = M; x.K = K;
+        x.A = B; x.lda = ldb; x.a = b == 'k' ? 'k' : 'm';
+        x.B = A; x.ldb = lda; x.b = a == 'k' ? 'k' : 'n';
+    } else {
+        x.M = M; x.N = N; x.K = K;
+        x.A = A; x.lda = lda; x.a = a;
+        x.B = B; x.ldb = ldb; x.b = b;
+    }
+    x.ldc = ldc;
+    const int es = kDtypes[dtype].in_bytes;
+    x.a_bytes = x.a == 'k' ? padded_extent(x.M, x.K, x.lda, es) : padded_extent(x.K, x.M, x.lda, es);
+    x.b_bytes = x.b == 'k' ? padded_extent(x.N, x.K, x.ldb, es) : padded_extent(x.K, x.N, x.ldb, es);
+    return x;
+}
+
+// ---------------------------------------------------------------- tuning table
+
+struct TuneEntry {
+    int dtype;
+    char a, b, c;
+    int64_t M, N, K;
+    int config;
+};
+
+std::mutex g_table_mu;
+std::vector<TuneEntry> g_table;
+std::once_flag g_env_once;
+
+int dtype_from_name(const std::string& s)
+{
+    for (int d = 0; d < GEMM_NUM_DTYPES; ++d)
+        if (s == kDtypes[d].name) return d;
+    return -1;
+}
+
+int parse_table(const char* path, std::vector<TuneEntry>& out)
+{
+    std::ifstream f(path);
+    if (!f) return GEMM_ERR_TUNING_FILE;
+    std::string line;
+    while (std::getline(f, line)) {
+        size_t hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::istringstream ss(line);
+        std::string dt, a, b, c;
+        int64_t M, N, K;
+        if (!(ss >> dt)) continue;  // blank line
+        if (!(ss >> a >> b >> c >> M >> N >> K)) return GEMM_ERR_TUNING_FILE;
+        std::string rest;
+        std::getline(ss, rest);
+        size_t s0 = rest.find_first_not_of(" \t");
+        size_t s1 = rest.find_last_not_of(" \t\r");
+        if (s0 == std::string::npos) return GEMM_ERR_TUNING_FILE;
+        std::string cfg = rest.substr(s0, s1 - s0 + 1);
+        int d = dtype_from_name(dt);
+        if (d < 0 || a.size() != 1 || b.size() != 1 || c.size() != 1 || M < 0 || N < 0 || K < 0)
+            return GEMM_ERR_TUNING_FILE;
+        int id = find_config(d, cfg);
+        if (id < 0) continue;       // a config this build does not have
+        out.push_back({d, (char)std::tolower(a[0]), (char)std::tolower(b[0]),
+                       (char)std::tolower(c[0]), M, N, K, id});
+    }
+    return GEMM_OK;
+}
+
+void load_env_table()
+{
+    const char* p = std::getenv("MI355_GEMM_TUNING");
+    if (!p || !*p) return;
+    std::vector<TuneEntry> t;
+    if (parse_table(p, t) == GEMM_OK) {
+        std::lock_guard<std::mutex> g(g_table_mu);
+        g_table.swap(t);
+    } else {
+        std::fprintf(stderr, "mi355_gemm: cannot read tuning table %s; using built-in choices\n", p);
+    }
+}
+
+// Built-in choice when the table has nothing for this dtype and layout.
+int heuristic(int dtype, int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    auto pick = [&](const char* tile) {
+        std::string name = std::string(kDtypes[dtype].name) + " " + tile;
+        int id = find_config(dtype, name);
+        return id < 0 ? 0 : id;
+    };
+    const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0);
+    if (dtype == GEMM_DTYPE_F32) {
+        if (tiles256 >= 512) return pick("256x256x16 w2x2 mfma32 s2 swz");
+        if (tiles256 >= 128) return pick("256x128x16 w2x2 mfma32 s2 swz");
+        if (M * N >= 512 * 512) return pick("128x128x16 w2x2 mfma32 s2 swz");
+        return pick("64x64x16 w2x2 mfma16 s2 swz");
+    }
+    if (tiles256 >= 256) return pick("256x256x64 w2x2 mfma32 s2 swz");
+    if (tiles256 >= 64) return pick("256x128x64 w2x2 mfma32 s2 swz");
+    if (M * N >= 512 * 512) return pick("128x128x64 w2x2 mfma32 s2 swz");
+    return pick("64x64x64 w2x2 mfma16 s2 swz");
+}
+
+int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
+{
+    std::call_once(g_env_once, load_env_table);
+    {
+        std::lock_guard<std::mutex> g(g_table_mu);
+        const TuneEntry* best = nullptr;
+        double best_d = 0;
+        for (const TuneEntry& e : g_table) {
+            if (e.dtype != dtype || e.a != a || e.b != b || e.c != c) continue;
+            if (e.M == M && e.N == N && e.K == K) return e.config;
+            double d = std::fabs(std::log2((double)std::max<int64_t>(M, 1) / std::max<int64_t>(e.M, 1))) +
+                       std::fabs(std::log2((double)std::max<int64_t>(N, 1) / std::max<int64_t>(e.N, 1))) +
+                       std::fabs(std::log2((double)std::max<int64_t>(K, 1) / std::max<int64_t>(e.K, 1)));
+            if (!best || d < best_d) { best = &e; best_d = d; }
+        }
+        if (best && best_d <= 1.0) return best->config;   // within a factor 2 overall
+    }
+    // The kernel only sees the canonical (C n-major) problem.
+    return c == 'm' ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
+}
+
+thread_local int t_last_config = -1;
+
+int launch(const Canon& x, int dtype, void* C, int config, void* stream)
+{
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    if (config < 0 || config >= n) return GEMM_ERR_NO_CONFIG;
+    const mg::KernelEntry& e = all[config];
+    const int es = kDtypes[dtype].in_bytes;
+    // Per-tile byte offsets are 32-bit: the rows a tile spans times the row
+    // pitch, plus the tile's extent along the contiguous index.
+    const int64_t a_span = ((x.a == 'k' ? e.BM : e.BK) * x.lda + std::max(e.BM, e.BK)) * es;
+    const int64_t b_span = ((x.b == 'k' ? e.BN : e.BK) * x.ldb + std::max(e.BN, e.BK)) * es;
+    if (a_span >= ((int64_t)1 << 31) || b_span >= ((int64_t)1 << 31)) return GEMM_ERR_BAD_SHAPE;
+    const int64_t tiles_m = (x.M + e.BM - 1) / e.BM, tiles_n = (x.N + e.BN - 1) / e.BN;
+    if (tiles_m * tiles_n >= ((int64_t)1 << 31)) return GEMM_ERR_BAD_SHAPE;
+
+    mg::Params p;
+    p.A = (const char*)x.A;
+    p.B = (const char*)x.B;
+    p.C = (char*)C;
+    p.M = (int)x.M; p.N = (int)x.N; p.K = (int)x.K;
+    p.tiles_m = (int)tiles_m; p.tiles_n = (int)tiles_n;
+    p.group_m = (int)std::min<int64_t>(8, tiles_m);
+    p.lda = x.lda; p.ldb = x.ldb; p.ldc = x.ldc;
+    p.a_bytes = x.K > 0 ? x.a_bytes : 0;
+    p.b_bytes = x.K > 0 ? x.b_bytes : 0;
+    const int layout = (x.a == 'k' ? 0 : 2) + (x.b == 'k' ? 0 : 1);
+    hipError_t err = e.launch(layout, p, (hipStream_t)stream);
+    if (err != hipSuccess) return GEMM_ERR_HIP;
+    t_last_config = config;
+    return GEMM_OK;
+}
+
+int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
+        const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config)
+{
+    t_last_config = -1;
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc);
+    if (st != GEMM_OK) return st;
+    if (config >= 0) {
+        int n = 0;
+        entries(dtype, &n);
+        if (config >= n) return GEMM_ERR_NO_CONFIG;
+    }
+    if (M == 0 || N == 0) return GEMM_OK;
+    Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc);
+    if (config < 0) config = select(dtype, a, b, c, M, N, K);
+    return launch(x, dtype, C, config, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major, int dtype,
+             const void* A, const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc,
+             void* stream)
+{
+    return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream, -1);
+}
+
+int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                    int dtype, const void* A, const void* B, void* C, int64_t lda, int64_t ldb,
+                    int64_t ldc, void* stream, int config_id)
+{
+    if (config_id < 0) {
+        t_last_config = -1;
+        return GEMM_ERR_NO_CONFIG;
+    }
+    return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream, config_id);
+}
+
+const char* gemm_status_str(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_BAD_SHAPE: return "bad shape: M, N or K negative or too large";
+    case GEMM_ERR_BAD_MAJOR: return "bad major: a in {k,m}, b in {k,n}, c in {n,m}";
+    case GEMM_ERR_BAD_DTYPE: return "bad dtype";
+    case GEMM_ERR_BAD_LD: return "bad leading dimension: smaller than the contiguous extent";
+    case GEMM_ERR_NULL_PTR: return "null pointer for an operand that is accessed";
+    case GEMM_ERR_MISALIGNED: return "misaligned: pointers and ld*element size must be 16-byte multiples";
+    case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_ERR_NO_CONFIG: return "no such tile config for this dtype";
+    case GEMM_ERR_HIP: return "HIP runtime error at launch";
+    case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
+    default: return "unknown status";
+    }
+}
+
+int gemm_num_configs(int dtype)
+{
+    int n = 0;
+    entries(dtype, &n);
+    return n;
+}
+
+int gemm_config_describe(int dtype, int config_id, char* buf, size_t len)
+{
+    if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return GEMM_ERR_BAD_DTYPE;
+    int n = 0;
+    const mg::KernelEntry* e = entries(dtype, &n);
+    if (config_id < 0 || config_id >= n || !buf || len == 0) return GEMM_ERR_NO_CONFIG;
+    std::snprintf(buf, len, "%s", e[config_id].name);
+    return GEMM_OK;
+}
+
+int gemm_select_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                       int dtype)
+{
+    // Shape/major/dtype checks only: pointers and leading dims play no part in the choice.
+    if (M < 0 || N < 0 || K < 0) return -GEMM_ERR_BAD_SHAPE;
+    char a = (char)std::tolower((unsigned char)a_major);
+    char b = (char)std::tolower((unsigned char)b_major);
+    char c = (char)std::tolower((unsigned char)c_major);
+    if ((a != 'k' && a != 'm') || (b != 'k' && b != 'n') || (c != 'n' && c != 'm'))
+        return -GEMM_ERR_BAD_MAJOR;
+    if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return -GEMM_ERR_BAD_DTYPE;
+    return select(dtype, a, b, c, M, N, K);
+}
+
+int gemm_last_config(void) { return t_last_config; }
+
+int gemm_load_tuning(const char* path)
+{
+    std::call_once(g_env_once, [] {});   // an explicit table wins over the environment
+    std::vector<TuneEntry> t;
+    if (path) {
+        int st = parse_table(path, t);
+        if (st != GEMM_OK) return st;
+    }
+    std::lock_guard<std::mutex> g(g_table_mu);
+    g_table.swap(t);
+    return GEMM_OK;
+}
+
+int gemm_tuning_size(void)
+{
+    std::lock_guard<std::mutex> g(g_table_mu);
+    return (int)g_table.size();
+}
+
+}  // extern "C"

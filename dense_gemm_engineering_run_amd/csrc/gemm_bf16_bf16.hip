@@ -1,0 +1,20 @@
+// Kernel instantiations for dtype bf16_bf16 (inputs BF16, output BF16).
+#include "gemm_kernel.hpp"
+#include "configs.def"
+
+namespace mg {
+
+#define MG_ENTRY(BM, BN, BK, WM, WN, MI, SWZ)                                        \
+    {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2" MG_SWZNAME_##SWZ, \
+     BM, BN, BK, WM, WN, MI, SWZ,                                                  \
+     &Inst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, SWZ>::launch},
+
+static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY)};
+
+const KernelEntry* entries_bf16_bf16(int* n)
+{
+    *n = (int)(sizeof(kEntries) / sizeof(kEntries[0]));
+    return kEntries;
+}
+
+}  // namespace mg

@@ -1,0 +1,455 @@
+// gemm_kernel.hpp -- gfx950 (CDNA4) MFMA GEMM kernel template.
+//
+// Computes C[m][n] = sum_k A[m][k] * B[n][k] with C row-major ("n"-major);
+// the host turns an m-major C into this form by computing C^T = B * A^T.
+// The operation, the M x K / N x K / M x N shapes and the k/m/n "major"
+// storage options are those of the CuTe DSL Ampere SGEMM example (module
+// docstring); the block tile / wave tile hierarchy is that of the CK Tile
+// practice GEMM README ("PracticeGemmShape Configuration").  The design below
+// is for CDNA4, not a translation of either page:
+//
+//  * Workgroup = WM x WN waves of 64 lanes; block tile BM x BN x BK; each wave
+//    owns a (BM/WM) x (BN/WN) sub-tile made of MI x MI MFMA tiles (MI = 32 or
+//    16).  fp32 inputs use v_mfma_f32_32x32x2_f32 / 16x16x4_f32; fp16 and
+//    bf16 use the gfx950 K-doubled v_mfma_f32_32x32x16_* / 16x16x32_*.
+//    Accumulation is fp32.
+//  * HBM -> LDS: every lane issues 128-bit buffer loads (buffer resource
+//    bounds checking returns zero outside the operand's extent).  Operands
+//    whose contiguous index is k are copied chunk by chunk; operands whose
+//    contiguous index is m (or n) are loaded as CE x CE blocks and transposed
+//    in registers, so LDS always holds k-contiguous rows and one MFMA inner
+//    loop serves all four layouts.
+//  * LDS: a ring of STAGES (2) buffers of [BM][BK] + [BN][BK]; 16-byte chunks
+//    are XOR-swizzled by row so that the 128-bit writes and the 128-bit
+//    fragment reads of a quarter-wave hit distinct banks (the SGEMM example
+//    pads rows for the same purpose).
+//  * Registers: the global loads of tile t+2 are issued while tile t is
+//    consumed and land in VGPRs that are written to LDS after the MFMAs of
+//    tile t+1's predecessor finish (one tile in flight per operand); the MFMA
+//    fragments of k-group g+1 are read from LDS while those of g are used.
+//  * fp32 operands: a lane reads 4 consecutive k of its row with one 128-bit
+//    LDS read and feeds them to 4 successive MFMAs; A and B use the same
+//    relabelling of k, so each element's sum is unchanged up to rounding
+//    order (the SGEMM example permutes its thread layout for vectorised
+//    shared-memory reads in the same spirit).
+//  * Edges: rows past M/N read zeros or padding that only reach C elements
+//    which are never stored; the partial last k-tile of a k-contiguous operand
+//    is masked to exact zeros in registers (both operands, so NaN padding
+//    cannot leak); C stores are predicated on m < M and n < N.
+//  * Workgroup -> tile: workgroups are dispatched round-robin over the 8 XCDs,
+//    so the linear id is remapped to give each XCD a contiguous range of the
+//    tile order, and that order walks groups of `group_m` tile rows column by
+//    column (L2 reuse inside one XCD).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum class In : int { F32 = 0, F16 = 1, BF16 = 2 };
+enum class Out : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Kernel arguments, already canonicalised to C n-major.
+struct Params {
+    const char* A;        // bytes
+    const char* B;
+    char* C;
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int group_m;          // tile rows per raster group
+    int64_t lda, ldb, ldc;  // elements
+    uint64_t a_bytes;     // readable extent of A / B in bytes
+    uint64_t b_bytes;
+};
+
+// Third dword of a buffer resource on gfx9-family parts: 32-bit data format,
+// raw (unswizzled) addressing.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, uint64_t bytes)
+{
+    uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, kBufferFlags);
+}
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <int CPR, bool SWZ>
+__device__ __forceinline__ int swz_chunk(int row, int c)
+{
+    if constexpr (!SWZ) {
+        return c;
+    } else {
+        // 128-byte bank window = 8 chunks of 16 B.  Rows shorter than the
+        // window share it; the XOR term walks over the chunks of the window.
+        constexpr int RPW = CPR >= 8 ? 1 : 8 / CPR;   // rows per window
+        constexpr int XM = CPR >= 8 ? 8 : CPR;        // xor range
+        return c ^ ((row / RPW) % XM);
+    }
+}
+
+// Masks the elements k >= K of a 16-byte chunk starting at element k0.
+template <In TI>
+__device__ __forceinline__ i32x4 mask_k(i32x4 v, int k0, int K)
+{
+    if constexpr (TI == In::F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (k0 + e >= K) v[e] = 0;
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t m = (k0 + 2 * d < K ? 0x0000ffffu : 0u) | (k0 + 2 * d + 1 < K ? 0xffff0000u : 0u);
+            v[d] = (int)((uint32_t)v[d] & m);
+        }
+    }
+    return v;
+}
+
+// Operand tile loader: ROWS x BK tile of an operand into LDS rows of BK.
+// KMAJ: the operand's contiguous index is k.
+template <In TI, int ROWS, int BK, int NT, bool KMAJ, bool SWZ>
+struct TileLoader {
+    static constexpr int ES = TI == In::F32 ? 4 : 2;   // element bytes
+    static constexpr int CE = 16 / ES;                  // elements per chunk
+    static constexpr int CPR = BK / CE;                 // chunks per LDS row
+    static constexpr int RB = BK * ES;                  // LDS row bytes
+    static constexpr int CHUNKS = ROWS * CPR;
+    static_assert(BK % CE == 0, "BK must be a multiple of the chunk");
+    static_assert(ROWS % CE == 0, "rows must be a multiple of the chunk");
+    // k-contiguous: one chunk per load; m-contiguous: CE x CE blocks.
+    static constexpr int UNITS = KMAJ ? CHUNKS : CHUNKS / CE;
+    static constexpr int PER = (UNITS + NT - 1) / NT;
+    static constexpr int REGS = KMAJ ? PER : PER * CE;  // i32x4 per thread
+    static constexpr bool FULL = UNITS % NT == 0;
+
+    i32x4 r[REGS];
+    int voff[PER];
+
+    // Precompute the per-thread byte offsets relative to the tile origin.
+    __device__ __forceinline__ void init(int tid, int64_t ld)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            int id = i * NT + tid;
+            if (KMAJ) {
+                int row = id / CPR, c = id % CPR;
+                voff[i] = (int)(row * ld * ES) + c * 16;
+            } else {
+                int kg = id % CPR, mc = id / CPR;
+                voff[i] = (int)(kg * CE * ld * ES) + mc * 16;
+            }
+        }
+        (void)ld;
+    }
+
+    // Issue the loads of the tile whose origin is (row0, k0).
+    __device__ __forceinline__ void load(const char* base, uint64_t bytes, int64_t ld, int row0,
+                                         int k0, int tid)
+    {
+        int64_t origin = KMAJ ? ((int64_t)row0 * ld + k0) * ES : ((int64_t)k0 * ld + row0) * ES;
+        uint64_t rem = (uint64_t)origin < bytes ? bytes - (uint64_t)origin : 0;
+        __amdgpu_buffer_rsrc_t rs = make_rsrc(base + origin, rem);
+        int ldb = (int)(ld * ES);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (FULL || i * NT + tid < UNITS) {
+                if (KMAJ) {
+                    r[i] = buf_load16(rs, voff[i]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < CE; ++j) r[i * CE + j] = buf_load16(rs, voff[i] + j * ldb);
+                }
+            }
+        }
+    }
+
+    // Zero k >= K in the loaded chunks (k-contiguous operands only; rows
+    // k >= K of an m-contiguous operand lie outside its extent and read 0).
+    __device__ __forceinline__ void mask(int k0, int K, int tid)
+    {
+        if constexpr (KMAJ) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                int id = i * NT + tid;
+                int c = id % CPR;
+                r[i] = mask_k<TI>(r[i], k0 + c * CE, K);
+            }
+        }
+    }
+
+    // Write the registers to LDS (k-contiguous rows, swizzled chunks).
+    __device__ __forceinline__ void store(char* lds, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            int id = i * NT + tid;
+            if (!(FULL || id < UNITS)) continue;
+            if (KMAJ) {
+                int row = id / CPR, c = id % CPR;
+                *(i32x4*)(lds + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16) = r[i];
+            } else {
+                int kg = id % CPR, mc = id / CPR;
+                // r[i*CE + j] holds k = kg*CE + j for m = mc*CE .. mc*CE+CE-1.
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    i32x4 o;
+                    if constexpr (ES == 4) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[j] = r[i * CE + j][e];
+                    } else {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            uint32_t lo = (uint32_t)r[i * CE + 2 * d][e >> 1];
+                            uint32_t hi = (uint32_t)r[i * CE + 2 * d + 1][e >> 1];
+                            if (e & 1) o[d] = (int)((lo >> 16) | (hi & 0xffff0000u));
+                            else o[d] = (int)((lo & 0xffffu) | (hi << 16));
+                        }
+                    }
+                    int row = mc * CE + e;
+                    *(i32x4*)(lds + row * RB + swz_chunk<CPR, SWZ>(row, kg) * 16) = o;
+                }
+            }
+        }
+    }
+};
+
+template <In TI, int MI>
+__device__ __forceinline__ void mfma_step(const i32x4& a, const i32x4& b, f32x16& acc)
+{
+    if constexpr (TI == In::F32) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[0]), __int_as_float(b[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[1]), __int_as_float(b[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[2]), __int_as_float(b[2]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[3]), __int_as_float(b[3]), acc, 0, 0, 0);
+    } else if constexpr (TI == In::F16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                     __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+    } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+}
+
+template <In TI, int MI>
+__device__ __forceinline__ void mfma_step(const i32x4& a, const i32x4& b, f32x4& acc)
+{
+    if constexpr (TI == In::F32) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[0]), __int_as_float(b[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[1]), __int_as_float(b[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[2]), __int_as_float(b[2]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[3]), __int_as_float(b[3]), acc, 0, 0, 0);
+    } else if constexpr (TI == In::F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                     __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+    } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+}
+
+template <Out TO>
+__device__ __forceinline__ void store_out(char* C, int64_t idx, float v)
+{
+    if constexpr (TO == Out::F32) {
+        ((float*)C)[idx] = v;
+    } else if constexpr (TO == Out::F16) {
+        ((_Float16*)C)[idx] = (_Float16)v;                       // round to nearest even
+    } else {
+        ((uint16_t*)C)[idx] = __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+    }
+}
+
+// Linear workgroup id -> (tile_m, tile_n).
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn)
+{
+    const int G = p.tiles_m * p.tiles_n;
+    const int w = blockIdx.x;
+    const int per = G / 8, rem = G % 8;
+    const int x = w % 8, idx = w / 8;
+    const int L = x * per + (x < rem ? x : rem) + idx;   // XCD x owns a contiguous range
+    const int width = p.group_m * p.tiles_n;
+    const int first = (L / width) * p.group_m;
+    const int gsz = min(p.tiles_m - first, p.group_m);
+    const int r = L % width;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_kernel(Params p)
+{
+    constexpr int NT = WM * WN * 64;
+    constexpr int ES = TI == In::F32 ? 4 : 2;
+    constexpr int CE = 16 / ES;
+    constexpr int CPR = BK / CE;
+    constexpr int RB = BK * ES;
+    constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
+    constexpr int TM = WTM / MI, TN = WTN / MI;      // MFMA tiles per wave
+    constexpr int NQ = 64 / MI;                      // lane groups along k
+    constexpr int NG = CPR / NQ;                     // k-groups per BK
+    constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be a multiple of the MFMA tile");
+    static_assert(CPR % NQ == 0, "BK too small for this MFMA shape");
+    static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+    using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    TileLoader<TI, BM, BK, NT, AK, SWZ> la;
+    TileLoader<TI, BN, BK, NT, BKM, SWZ> lb;
+    la.init(tid, p.lda);
+    lb.init(tid, p.ldb);
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = Acc{};
+
+    const int nkt = (p.K + BK - 1) / BK;
+    const bool ragged = (p.K % BK) != 0;
+
+    // Fragment read: row r of the wave's operand sub-tile, k-group g.
+    const int frow = lane % MI;
+    const int fq = lane / MI;
+
+    if (nkt > 0) {
+        la.load(p.A, p.a_bytes, p.lda, m0, 0, tid);
+        lb.load(p.B, p.b_bytes, p.ldb, n0, 0, tid);
+        if (nkt == 1 && ragged) { la.mask(0, p.K, tid); lb.mask(0, p.K, tid); }
+        la.store(smem, tid);
+        lb.store(smem + A_BYTES, tid);
+        if (nkt > 1) {
+            la.load(p.A, p.a_bytes, p.lda, m0, BK, tid);
+            lb.load(p.B, p.b_bytes, p.ldb, n0, BK, tid);
+        }
+        __syncthreads();
+    }
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const char* sa = smem + (kt & 1) * STAGE;
+        const char* sb = sa + A_BYTES;
+
+        i32x4 fa[2][TM], fb[2][TN];
+        auto read_frags = [&](int g, int buf) {
+            const int c = g * NQ + fq;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                int row = wm * WTM + i * MI + frow;
+                fa[buf][i] = *(const i32x4*)(sa + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                int row = wn * WTN + j * MI + frow;
+                fb[buf][j] = *(const i32x4*)(sb + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
+            }
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) read_frags(g + 1, (g + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    mfma_step<TI, MI>(fa[g & 1][i], fb[g & 1][j], acc[i][j]);
+        }
+
+        if (kt + 1 < nkt) {
+            if (kt + 1 == nkt - 1 && ragged) {
+                la.mask((kt + 1) * BK, p.K, tid);
+                lb.mask((kt + 1) * BK, p.K, tid);
+            }
+            char* nxt = smem + ((kt + 1) & 1) * STAGE;
+            la.store(nxt, tid);
+            lb.store(nxt + A_BYTES, tid);
+            if (kt + 2 < nkt) {
+                la.load(p.A, p.a_bytes, p.lda, m0, (kt + 2) * BK, tid);
+                lb.load(p.B, p.b_bytes, p.ldb, n0, (kt + 2) * BK, tid);
+            }
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: fp32 accumulators -> output type, predicated stores.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * WTN + j * MI + (lane % MI);
+            const int mb = m0 + wm * WTM + i * MI;
+            if constexpr (MI == 32) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = mb + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mb + (lane / 16) * 4 + r;
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+// One tile configuration, instantiated for the four operand layouts.
+using LaunchFn = hipError_t (*)(int layout, const Params& p, hipStream_t s);
+
+struct KernelEntry {
+    const char* name;
+    int BM, BN, BK, WM, WN, MI;
+    bool swz;
+    LaunchFn launch;
+};
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>
+struct Inst {
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WM * WN * 64);
+        switch (layout) {
+        case 0: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, true, true, SWZ><<<grid, block, 0, s>>>(p); break;
+        case 1: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, true, false, SWZ><<<grid, block, 0, s>>>(p); break;
+        case 2: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, false, true, SWZ><<<grid, block, 0, s>>>(p); break;
+        default: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, false, false, SWZ><<<grid, block, 0, s>>>(p); break;
+        }
+        return hipGetLastError();
+    }
+};
+
+// Per-dtype registries, defined in the gemm_<dtype>.hip files.
+const KernelEntry* entries_f32(int* n);
+const KernelEntry* entries_f16_f32(int* n);
+const KernelEntry* entries_bf16_bf16(int* n);
+const KernelEntry* entries_f16_f16(int* n);
+const KernelEntry* entries_bf16_f32(int* n);
+
+}  // namespace mg

@@ -1,0 +1,146 @@
+/*
+ * mi355_gemm.h -- C ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * Operation (CuTe DSL Ampere SGEMM example, module docstring and the
+ * einsum('mk,nk->mn') reference check in run(); CK Tile practice GEMM README,
+ * "Host Matrix Creation"):
+ *
+ *     C[m][n] = sum over k < K of A[m][k] * B[n][k]
+ *
+ * with A logically M x K, B logically N x K and C logically M x N.  C is
+ * overwritten and never read (the SGEMM example's epilogue is the identity
+ * and the initial contents of C are discarded).  Products are formed exactly
+ * and accumulated in fp32 on the MFMA units; the summation order is the
+ * library's own.
+ *
+ * Storage.  Each matrix has one contiguous ("major") index, as in the SGEMM
+ * example's --a_major / --b_major / --c_major flags and its
+ * create_and_permute_tensor():
+ *     a_major 'k': A[m][k] at A + m*lda + k     'm': at A + m + k*lda
+ *     b_major 'k': B[n][k] at B + n*ldb + k     'n': at B + n + k*ldb
+ *     c_major 'n': C[m][n] at C + m*ldc + n     'm': at C + m + n*ldc
+ * Major characters are case-insensitive.  Leading dimensions and sizes are in
+ * ELEMENTS.  All pointers are device pointers (HBM), owned by the caller; the
+ * library keeps no pointer after a call returns and allocates nothing.
+ *
+ * Alignment (SGEMM example, "Constraints" in its docstring: the contiguous
+ * dimension must be at least 16-byte aligned): A, B and C must be 16-byte
+ * aligned and ld * sizeof(element) must be a multiple of 16.  Each operand
+ * must be readable (C: writable) over its padded extent: for A k-major,
+ * (M-1)*lda elements plus K rounded up to a 16-byte multiple; likewise for
+ * the other majors.  The ld padding may hold anything, NaN included: it never
+ * reaches C.  C's padding is never written.
+ *
+ * Asynchrony.  gemm_run only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns.  The caller synchronises.  Launch errors
+ * are reported as GEMM_ERR_HIP; faults inside a kernel surface at the
+ * caller's synchronisation.
+ *
+ * Errors.  Every function returns a status and never throws.  All argument
+ * checks run before any HIP call, in the order of gemm_status_t below, so
+ * they can be exercised without a GPU.
+ *
+ * Degenerate sizes.  M == 0 or N == 0: nothing is launched, GEMM_OK.
+ * K == 0: C is filled with zeros (the empty sum); A and B are not read.
+ *
+ * Threads.  All functions are reentrant.  The only global state is the tuning
+ * table, guarded by a mutex, and a per-thread record of the last config.
+ */
+#ifndef MI355_GEMM_H
+#define MI355_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input type -> output type; accumulation is always fp32. */
+typedef enum {
+    GEMM_DTYPE_F32 = 0,        /* A, B fp32 -> C fp32                         */
+    GEMM_DTYPE_F16_F32 = 1,    /* A, B fp16 -> C fp32                         */
+    GEMM_DTYPE_BF16_BF16 = 2,  /* A, B bf16 -> C bf16 (round to nearest even) */
+    GEMM_DTYPE_F16_F16 = 3,    /* A, B fp16 -> C fp16 (round to nearest even) */
+    GEMM_DTYPE_BF16_F32 = 4,   /* A, B bf16 -> C fp32                         */
+    GEMM_NUM_DTYPES = 5
+} gemm_dtype_t;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_BAD_SHAPE = 1,    /* M, N or K negative, or a size too large for 32-bit tile indexing */
+    GEMM_ERR_BAD_MAJOR = 2,    /* major character not in {k,m} / {k,n} / {n,m}          */
+    GEMM_ERR_BAD_DTYPE = 3,    /* dtype not a gemm_dtype_t                               */
+    GEMM_ERR_BAD_LD = 4,       /* ld smaller than the contiguous extent (or than 1)      */
+    GEMM_ERR_NULL_PTR = 5,     /* A or B NULL while M*N*K > 0, or C NULL while M*N > 0   */
+    GEMM_ERR_MISALIGNED = 6,   /* pointer not 16-byte aligned, or ld*elem not 16-byte multiple */
+    GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */
+    GEMM_ERR_NO_CONFIG = 8,    /* config id out of range for this dtype                  */
+    GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
+    GEMM_ERR_TUNING_FILE = 10  /* tuning table missing or malformed                      */
+} gemm_status_t;
+
+/*
+ * C = A * B^T (storage B is N x K) as described above, with the tile config
+ * chosen from the tuning table (exact key match, else the nearest tuned shape
+ * of the same dtype and layout, else a built-in heuristic).
+ */
+int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+             int dtype, const void* A, const void* B, void* C,
+             int64_t lda, int64_t ldb, int64_t ldc, void* stream);
+
+/*
+ * Same as gemm_run but with an explicit tile config (0 <= config_id <
+ * gemm_num_configs(dtype)).  Used by the offline tuner and by the tests that
+ * cover every config; GEMM_ERR_NO_CONFIG when the id is out of range.
+ */
+int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                    int dtype, const void* A, const void* B, void* C,
+                    int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config_id);
+
+/* Static description of a status code; never NULL. */
+const char* gemm_status_str(int status);
+
+/* Number of tile configs built for `dtype` (0 for an unknown dtype). */
+int gemm_num_configs(int dtype);
+
+/*
+ * Writes a NUL-terminated description of config `config_id` of `dtype` into
+ * buf (at most len bytes, truncated): its name, e.g.
+ * "f16 256x256x64 w2x2 mfma32 s2 swz".  Returns GEMM_OK, GEMM_ERR_BAD_DTYPE or
+ * GEMM_ERR_NO_CONFIG (also when buf is NULL or len is 0).
+ */
+int gemm_config_describe(int dtype, int config_id, char* buf, size_t len);
+
+/*
+ * The config id gemm_run would launch for these arguments (after the
+ * C-m-major swap and the table lookup), or a negative gemm_status_t negated
+ * when the arguments are invalid.  Host only: no HIP call.
+ */
+int gemm_select_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major,
+                       char c_major, int dtype);
+
+/*
+ * Config id launched by the calling thread's last successful gemm_run /
+ * gemm_run_config (-1 if none, or if that call launched no GEMM kernel).
+ * Lets a tuner verify that the kernel it timed is the candidate it asked for.
+ */
+int gemm_last_config(void);
+
+/*
+ * Replace the tuning table with the one in `path` (text; one entry per line:
+ * "dtype a_major b_major c_major M N K config_name", '#' starts a comment).
+ * path NULL clears the table.  Entries naming unknown configs are skipped.
+ * Returns GEMM_OK or GEMM_ERR_TUNING_FILE (the old table is then kept).  The
+ * table is also read once, at the first call, from $MI355_GEMM_TUNING if set.
+ */
+int gemm_load_tuning(const char* path);
+
+/* Number of entries in the current tuning table. */
+int gemm_tuning_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_GEMM_H */

@@ -1,0 +1,155 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, and rejects bad arguments before touching the HIP runtime.  Config
+selection and the tuning table are host logic and are covered here too."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_engineering_run_amd as g
+from dense_gemm_engineering_run_amd import _binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355_gemm.h")
+
+NULL = 0
+P = 1 << 20          # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "gemm_run" in names and len(names) >= 9
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in range(11):
+        s = g.gemm_status_str(st)
+        assert s and s != "unknown status"
+    assert g.gemm_status_str(99) == "unknown status"
+
+
+def run(M=64, N=64, K=64, a="k", bm="k", c="n", dtype=0, A=P, B=2 * P, C=3 * P, lda=None,
+        ldb=None, ldc=None):
+    lda = lda if lda is not None else (K if a in "kK" else M)
+    ldb = ldb if ldb is not None else (K if bm in "kK" else N)
+    ldc = ldc if ldc is not None else (N if c in "nN" else M)
+    return g.gemm_run(M, N, K, a, bm, c, dtype, A, B, C, lda, ldb, ldc, 0)
+
+
+def test_validation_errors_without_gpu():
+    assert run(M=-1) == b.GEMM_ERR_BAD_SHAPE
+    assert run(K=-5) == b.GEMM_ERR_BAD_SHAPE
+    assert run(M=1 << 31) == b.GEMM_ERR_BAD_SHAPE
+    assert run(a="n") == b.GEMM_ERR_BAD_MAJOR
+    assert run(bm="m") == b.GEMM_ERR_BAD_MAJOR
+    assert run(c="k") == b.GEMM_ERR_BAD_MAJOR
+    assert run(dtype=5) == b.GEMM_ERR_BAD_DTYPE
+    assert run(dtype=-1) == b.GEMM_ERR_BAD_DTYPE
+    assert run(lda=63) == b.GEMM_ERR_BAD_LD
+    assert run(a="m", lda=32) == b.GEMM_ERR_BAD_LD
+    assert run(ldc=0, N=0) == b.GEMM_ERR_BAD_LD           # ld must be >= 1
+    assert run(A=NULL) == b.GEMM_ERR_NULL_PTR
+    assert run(B=NULL) == b.GEMM_ERR_NULL_PTR
+    assert run(C=NULL) == b.GEMM_ERR_NULL_PTR
+    assert run(A=P + 4) == b.GEMM_ERR_MISALIGNED
+    assert run(C=3 * P + 8) == b.GEMM_ERR_MISALIGNED
+    assert run(K=30, lda=30, ldb=32) == b.GEMM_ERR_MISALIGNED   # 30 * 4 bytes
+    assert run(K=60, dtype=1, lda=60, ldb=64) == b.GEMM_ERR_MISALIGNED  # 120 bytes
+    assert run(C=P + 64 * 16) == b.GEMM_ERR_ALIAS          # C starts inside A
+    assert run(C=P - 64 * 64 * 4 + 16) == b.GEMM_ERR_ALIAS  # C ends inside A
+    assert run(lda=63, a="x") == b.GEMM_ERR_BAD_MAJOR       # checks run in header order
+    assert g.gemm_last_config() == -1
+
+
+def test_degenerate_sizes_without_gpu():
+    # M == 0 or N == 0: no launch, OK; pointers may be NULL.
+    assert run(M=0, A=NULL, B=NULL, C=NULL) == b.GEMM_OK
+    assert run(N=0, A=NULL, B=NULL, C=NULL, ldc=4) == b.GEMM_OK
+    # K == 0 needs no A/B (but does need C): the NULL checks reflect that.
+    assert run(K=0, A=NULL, B=NULL, C=NULL, lda=1, ldb=1) == b.GEMM_ERR_NULL_PTR
+    assert g.gemm_last_config() == -1
+
+
+def test_majors_case_insensitive():
+    assert run(a="X") == b.GEMM_ERR_BAD_MAJOR
+    assert run(M=0, a="K", bm="N", c="M", ldc=4) == b.GEMM_OK
+
+
+def test_config_registry():
+    for d in range(5):
+        n = g.gemm_num_configs(d)
+        assert n >= 3
+        names = [g.gemm_config_describe(d, i) for i in range(n)]
+        assert len(set(names)) == n
+        assert all(nm.startswith(b.DTYPE_NAMES[d] + " ") for nm in names)
+        with pytest.raises(b.GemmError):
+            g.gemm_config_describe(d, n)
+    assert g.gemm_num_configs(7) == 0
+    buf = ctypes.create_string_buffer(8)
+    assert b._lib.gemm_config_describe(0, 0, buf, 8) == b.GEMM_OK and len(buf.value) == 7
+    assert g.gemm_run_config(64, 64, 64, "k", "k", "n", 0, P, 2 * P, 3 * P, 64, 64, 64, 0,
+                             999) == b.GEMM_ERR_NO_CONFIG
+    assert g.gemm_run_config(64, 64, 64, "k", "k", "n", 0, P, 2 * P, 3 * P, 64, 64, 64, 0,
+                             -1) == b.GEMM_ERR_NO_CONFIG
+
+
+def test_select_config_is_host_logic():
+    for d in range(5):
+        for shape in [(1, 1, 1), (1024, 512, 256), (8192, 8192, 8192), (65536, 256, 4096)]:
+            for c in "nm":
+                cfg = g.gemm_select_config(*shape, "k", "k", c, d)
+                assert 0 <= cfg < g.gemm_num_configs(d)
+    assert g.gemm_select_config(-1, 1, 1, "k", "k", "n", 0) == -b.GEMM_ERR_BAD_SHAPE
+    assert g.gemm_select_config(1, 1, 1, "q", "k", "n", 0) == -b.GEMM_ERR_BAD_MAJOR
+    assert g.gemm_select_config(1, 1, 1, "k", "k", "n", 9) == -b.GEMM_ERR_BAD_DTYPE
+
+
+def test_tuning_table_lookup(tmp_path):
+    saved = g.gemm_tuning_size()
+    name0 = g.gemm_config_describe(0, 0)
+    name2 = g.gemm_config_describe(0, 2)
+    t = tmp_path / "t.txt"
+    t.write_text(f"# comment\n\nf32 k k n 1000 1000 1000 {name2}\n"
+                 f"f32 m n n 8192 8192 8192 {name0}   # trailing comment\n"
+                 f"f32 k k n 5 5 5 f32 no such config\n")
+    try:
+        assert g.gemm_load_tuning(str(t)) == b.GEMM_OK
+        assert g.gemm_tuning_size() == 2            # the unknown config is skipped
+        assert g.gemm_select_config(1000, 1000, 1000, "k", "k", "n", 0) == 2   # exact
+        assert g.gemm_select_config(1100, 900, 1000, "k", "k", "n", 0) == 2    # nearest
+        assert g.gemm_select_config(8192, 8192, 8192, "m", "n", "n", 0) == 0
+        bad = tmp_path / "bad.txt"
+        bad.write_text("f32 k k n 10 10\n")
+        assert g.gemm_load_tuning(str(bad)) == b.GEMM_ERR_TUNING_FILE
+        assert g.gemm_tuning_size() == 2                                        # kept
+        assert g.gemm_load_tuning(str(tmp_path / "missing.txt")) == b.GEMM_ERR_TUNING_FILE
+        assert g.gemm_load_tuning(None) == b.GEMM_OK and g.gemm_tuning_size() == 0
+    finally:
+        if os.path.exists(b.DEFAULT_TABLE):
+            g.gemm_load_tuning(b.DEFAULT_TABLE)
+        else:
+            g.gemm_load_tuning(None)
+    assert g.gemm_tuning_size() == saved
+
+
+def test_torch_helper_derives_majors_from_strides():
+    torch = pytest.importorskip("torch")
+    a = torch.empty(64, 40)                      # (M, K) row-major -> 'k', lda 40
+    assert b._major(a, "m", "k") == ("k", 40)
+    at = torch.empty(40, 72)[:, :64].t()         # (M, K) view of column storage, ld 72
+    assert b._major(at, "m", "k") == ("m", 72)
+    with pytest.raises(ValueError):
+        b._major(torch.empty(8, 8)[::2, ::2], "m", "k")
+    assert b.dtype_code(torch.float16, torch.float32) == b.DTYPE_F16_F32
+    with pytest.raises(ValueError):
+        b.dtype_code(torch.float64, torch.float64)

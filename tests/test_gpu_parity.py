@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Workloads (seeded, synthetic; see gemm_inputs):
+  1. fp32 1024x512x256, A k-major, B k-major, C n-major, integers in [-5,5]   -> bit-exact
+  2. fp32 8192^3, A m-major, B n-major, C n-major, uniform(-1,1)             -> normwise <= 1e-5
+  3. fp16 4096^3 -> fp32, all 8 layouts, normal(0,1)                         -> normwise <= 1e-5
+  4. fp32 4095x2049x1028 ragged, A k, B k, C n (ldc 2052), uniform(-1,1)     -> normwise <= 1e-5
+  5. bf16 65536x256x4096 -> bf16, A k, B k, C n, normal(0,0.02)              -> normwise <= 8e-3
+Integer-valued inputs at each shape must match bit for bit.  Large shapes are
+compared on sampled row blocks (all columns), small ones in full.
+"""
+import itertools
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+import gemm_inputs as gi  # noqa: E402
+import gpu_util as gu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS8 = [(a, b, c) for a in "km" for b in "kn" for c in "nm"]
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def full_check(prob, exact, config=None):
+    c, flat, st = gu.run(prob, config=config)
+    assert st == 0, st
+    ref = gu.reference(prob)
+    ok, info = gu.check(c, ref, prob, exact)
+    assert ok, info
+    assert gu.padding_intact(flat, prob)
+    return info
+
+
+def sampled_check(prob, exact, dev=None, blocks=None, c=None):
+    if c is None:
+        c, flat, st = gu.run(prob, dev=dev)
+        assert st == 0, st
+        assert gu.padding_intact(flat, prob)
+    blocks = blocks or gu.sample_blocks(prob["M"])
+    refs = [gu.reference(prob, rows=b) for b in blocks]
+    got = np.concatenate([c[b0:b1] for b0, b1 in blocks])
+    ok, info = gu.check(got, np.concatenate(refs), prob, exact)
+    assert ok, (blocks, info)
+    return info
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_w1_fp32_1024x512x256_integer_exact():
+    log("w1 fp32 1024x512x256 kkn int5")
+    prob = gi.problem(1024, 512, 256, "k", "k", "n", "f32", "int5")
+    full_check(prob, exact=True)
+
+
+@pytest.mark.parametrize("kind,exact", [("u11", False), ("int5", True)])
+def test_w2_fp32_8192_cube(kind, exact):
+    log(f"w2 fp32 8192^3 mnn {kind}")
+    prob = gi.problem(8192, 8192, 8192, "m", "n", "n", "f32", kind)
+    info = sampled_check(prob, exact)
+    log(f"  {info}")
+
+
+@pytest.mark.parametrize("kind,exact", [("n01", False), ("int5", True)])
+def test_w3_fp16_4096_cube_all_layouts(kind, exact):
+    M = N = K = 4096
+    a_log, b_log = gi.draw_ab(M, N, K, kind)
+    a16, b16 = gi.cast(a_log, "f16"), gi.cast(b_log, "f16")
+    blocks = gu.sample_blocks(M)
+    refs = None
+    for am, bm, cm in LAYOUTS8:
+        log(f"w3 fp16 4096^3 {am}{bm}{cm} {kind}")
+        prob = dict(M=M, N=N, K=K, a_major=am, b_major=bm, c_major=cm, dtype=1, in_type="f16",
+                    out_type="f32", lda=4096, ldb=4096, ldc=4096, c_first=(cm == "m"),
+                    A=gi.store(a16, am == "m", 4096), B=gi.store(b16, bm == "n", 4096))
+        c, flat, st = gu.run(prob)
+        assert st == 0
+        if refs is None:  # same logical inputs for every layout: compute the oracle once
+            refs = np.concatenate([gu.reference(prob, rows=b) for b in blocks])
+        got = np.concatenate([c[b0:b1] for b0, b1 in blocks])
+        ok, info = gu.check(got, refs, prob, exact)
+        assert ok, (am, bm, cm, info)
+        log(f"  {info}")
+
+
+@pytest.mark.parametrize("kind,exact", [("u11", False), ("int5", True)])
+def test_w4_fp32_ragged(kind, exact):
+    log(f"w4 fp32 4095x2049x1028 kkn {kind}")
+    prob = gi.problem(4095, 2049, 1028, "k", "k", "n", "f32", kind, ldc=2052)
+    info = full_check(prob, exact)
+    log(f"  {info}")
+
+
+@pytest.mark.parametrize("kind,exact", [("n002", False), ("int5", True)])
+def test_w5_bf16_tall_skinny(kind, exact):
+    log(f"w5 bf16 65536x256x4096 kkn {kind}")
+    prob = gi.problem(65536, 256, 4096, "k", "k", "n", "bf16_bf16", kind)
+    info = sampled_check(prob, exact, blocks=gu.sample_blocks(65536, size=64))
+    log(f"  {info}")
+
+
+# ---------------------------------------------------------------- edges and configs
+
+EDGE = [1, 2, 3, 15, 16, 17, 31, 33, 63, 65, 127, 129, 255, 257]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_edge_sizes_integer_exact(dtype):
+    rng = np.random.Generator(np.random.PCG64(sum(map(ord, dtype))))
+    triples = [(int(rng.choice(EDGE)), int(rng.choice(EDGE)), int(rng.choice(EDGE)))
+               for _ in range(6)] + [(1, 1, 1), (257, 255, 1), (3, 129, 257)]
+    for (M, N, K), (am, bm, cm) in itertools.product(triples, LAYOUTS8):
+        prob = gi.problem(M, N, K, am, bm, cm, dtype, "int5", seed=M * 7 + N * 3 + K)
+        c, flat, st = gu.run(prob)
+        assert st == 0
+        ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
+        assert ok, (dtype, M, N, K, am, bm, cm, info)
+        assert gu.padding_intact(flat, prob), (dtype, M, N, K, am, bm, cm)
+    log(f"{dtype}: {len(triples) * 8} edge cases exact")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_every_config_every_layout(dtype):
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    for cfg in range(g.gemm_num_configs(code)):
+        name = g.gemm_config_describe(code, cfg)
+        for am, bm, cm in LAYOUTS8:
+            prob = gi.problem(300, 200, 136, am, bm, cm, dtype, "int5", seed=cfg)
+            c, flat, st = gu.run(prob, config=cfg)
+            assert st == 0
+            assert g.gemm_last_config() == cfg
+            ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
+            assert ok, (name, am, bm, cm, info)
+        log(f"{name}: 8 layouts exact")
+
+
+def test_every_config_nonintegers_multi_tile():
+    import dense_gemm_engineering_run_amd as g
+    for dtype, kind in [("f32", "u11"), ("f16_f32", "n01"), ("bf16_bf16", "n002")]:
+        code = gi.DTYPE_CODE[dtype]
+        prob = gi.problem(515, 777, 333, "m", "k", "n", dtype, kind, seed=3)
+        ref = gu.reference(prob)
+        for cfg in range(g.gemm_num_configs(code)):
+            c, _, st = gu.run(prob, config=cfg)
+            assert st == 0
+            ok, info = gu.check(c, ref, prob, exact=False)
+            assert ok, (g.gemm_config_describe(code, cfg), info)
+
+
+# ---------------------------------------------------------------- canaries and edge semantics
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
+def test_nan_in_ld_padding_does_not_reach_c(dtype):
+    for am, bm, cm in LAYOUTS8:
+        prob = gi.problem(130, 67, 77, am, bm, cm, dtype, "int5", seed=9,
+                          lda=(136 if am == "m" else 88), ldb=(72 if bm == "n" else 88),
+                          ldc=(136 if cm == "m" else 72), pad_fill=float("nan"))
+        c, flat, st = gu.run(prob)
+        assert st == 0
+        ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
+        assert ok, (am, bm, cm, info)
+        assert gu.padding_intact(flat, prob)
+
+
+def test_deterministic_bitwise():
+    prob = gi.problem(1000, 700, 900, "m", "k", "n", "f32", "u11", seed=4)
+    c1, _, _ = gu.run(prob)
+    c2, _, _ = gu.run(prob)
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
+def test_nondefault_stream():
+    import torch
+    s = torch.cuda.Stream()
+    prob = gi.problem(500, 300, 200, "k", "n", "m", "f16_f32", "int5", seed=2)
+    with torch.cuda.stream(s):
+        c, _, st = gu.run(prob, stream=s)
+    assert st == 0
+    ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16"])
+def test_k_zero_gives_zeros_and_empty_is_noop(dtype):
+    prob = gi.problem(70, 50, 0, "k", "k", "n", dtype, "int5")
+    c, flat, st = gu.run(prob)
+    assert st == 0
+    assert np.all(gu.compare.as_f64(c, prob["out_type"]) == 0)
+    assert gu.padding_intact(flat, prob)
+    for M, N in [(0, 50), (70, 0)]:
+        prob = gi.problem(M, N, 16, "k", "k", "n", dtype, "int5")
+        _, flat, st = gu.run(prob)
+        assert st == 0
+        got = flat.view(np.uint32 if prob["out_type"] == "f32" else np.uint16)
+        assert np.all(got == gu.SENTINEL[prob["out_type"]])      # C untouched
+
+
+def test_large_integer_sums_stay_exact():
+    # K * 25 < 2^24: every fp32 partial sum is an exact integer.
+    prob = gi.problem(64, 96, 20000, "k", "n", "n", "f32", "int5", seed=12)
+    full_check(prob, exact=True)
