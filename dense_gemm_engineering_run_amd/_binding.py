@@ -17,7 +17,34 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build the HIP library first "
         "(python -m dense_gemm_engineering_run_amd.build, or __graft_entry__.build())")
 
+# PyTorch (used for device memory and streams) ships its own HIP runtime with
+# the same SONAME as /opt/rocm's.  Loading torch first makes the library bind
+# to that one copy; loading the library first would leave two HIP runtimes in
+# the process and kernel launches on torch's memory would fail.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split()[-1]
+                if "libamdhip64.so" in os.path.basename(p):
+                    paths.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded ({_hip_runtimes()}); import torch before any "
+                      "other HIP library, or load this package first")
 
 _i64, _int, _chr, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_char, ctypes.c_void_p
 _RUN_ARGS = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]

@@ -432,16 +432,24 @@ struct KernelEntry {
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>
 struct Inst {
+    template <bool AK, bool BKM>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        // hipLaunchKernel reports this launch's own status (a stale error left
+        // by an earlier runtime call on the thread cannot be mistaken for it).
+        Params copy = p;
+        void* args[] = {&copy};
+        return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>,
+                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+    }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {
-        dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WM * WN * 64);
         switch (layout) {
-        case 0: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, true, true, SWZ><<<grid, block, 0, s>>>(p); break;
-        case 1: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, true, false, SWZ><<<grid, block, 0, s>>>(p); break;
-        case 2: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, false, true, SWZ><<<grid, block, 0, s>>>(p); break;
-        default: gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, false, false, SWZ><<<grid, block, 0, s>>>(p); break;
+        case 0: return go<true, true>(p, s);
+        case 1: return go<true, false>(p, s);
+        case 2: return go<false, true>(p, s);
+        default: return go<false, false>(p, s);
         }
-        return hipGetLastError();
     }
 };
 

@@ -172,8 +172,11 @@ def test_nan_in_ld_padding_does_not_reach_c(dtype):
 
 def test_deterministic_bitwise():
     prob = gi.problem(1000, 700, 900, "m", "k", "n", "f32", "u11", seed=4)
-    c1, _, _ = gu.run(prob)
-    c2, _, _ = gu.run(prob)
+    c1, _, st1 = gu.run(prob)
+    c2, _, st2 = gu.run(prob)
+    assert st1 == 0 and st2 == 0
+    ok, info = gu.check(c1, gu.reference(prob), prob, exact=False)
+    assert ok, info
     assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
 
 
