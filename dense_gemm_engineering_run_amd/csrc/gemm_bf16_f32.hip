@@ -1,5 +1,5 @@
 // Kernel instantiations for dtype bf16_f32 (inputs BF16, output F32).
-#include "gemm_kernel.hpp"
+#include "gemm_dma.hpp"
 #include "configs.def"
 
 namespace mg {
@@ -7,9 +7,14 @@ namespace mg {
 #define MG_ENTRY(BM, BN, BK, WM, WN, MI, SWZ)                                        \
     {"bf16_f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2" MG_SWZNAME_##SWZ, \
      BM, BN, BK, WM, WN, MI, SWZ,                                                  \
-     &Inst<In::BF16, Out::F32, BM, BN, BK, WM, WN, MI, SWZ>::launch},
+     &Inst<In::BF16, Out::F32, BM, BN, BK, WM, WN, MI, SWZ>::launch, 2, false},
 
-static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY)};
+#define MG_DMA_ENTRY(BM, BN, BK, WM, WN, MI, ST)                                      \
+    {"bf16_f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s" #ST " dma",          \
+     BM, BN, BK, WM, WN, MI, true,                                                  \
+     &DmaInst<In::BF16, Out::F32, BM, BN, BK, WM, WN, MI, ST>::launch, ST, true},
+
+static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)};
 
 const KernelEntry* entries_bf16_f32(int* n)
 {

@@ -1,0 +1,349 @@
+// gemm_dma.hpp -- gfx950 GEMM for 16-bit inputs with direct HBM -> LDS loads.
+//
+// Same operation and canonical form as gemm_kernel.hpp (C = A * B^T with C
+// n-major; CuTe DSL Ampere SGEMM example, module docstring).  This variant is
+// built around two gfx950 instructions:
+//
+//  * buffer_load_dwordx4 ... lds: each lane's 16 bytes go straight from HBM
+//    into LDS at (M0 + 16 * lane), with no VGPR staging and no LDS write
+//    instruction.  Bounds checking of the buffer resource writes zeros for
+//    out-of-range lanes.  The loads of one k-tile for both operands are issued
+//    STAGES-1 tiles ahead into a ring of STAGES LDS buffers (the multistage
+//    shared-memory pipeline of the SGEMM example, mainloop comment), so several
+//    hundred KB per CU are in flight and the one barrier per k-tile both
+//    publishes tile t and frees the stage that tile t-1 used.
+//  * ds_read_b64_tr_b16: a transposing LDS read.  Within each 16-lane group,
+//    lane j receives element (j mod 4) of the 8-byte values addressed by lanes
+//    4r + j/4, r = 0..3.  When lane s addresses row k0 + s/4, column
+//    m0 + 4 (s mod 4) of an m-contiguous tile, lane j receives
+//    A[k0 + r][m0 + j] for r = 0..3: four consecutive k of one row, the MFMA
+//    operand order.  Operands whose contiguous index is m (or n) therefore
+//    stay m-contiguous in LDS and are transposed on the read.
+//
+// LDS layouts (16-byte chunks XOR-swizzled for gfx950's 256-byte bank window):
+//  k-contiguous operand: [ROWS][BK]; 16 lanes reading one logical chunk of 16
+//    consecutive rows hit 16 distinct bank positions (as in gemm_kernel.hpp).
+//  m-contiguous operand: [BK][ROWS]; a transposing read touches 4 rows x 64 B
+//    per 32 lanes, so row k's chunks are XORed with 4 * (k mod 4) (rows sharing
+//    a window) to spread those 4 rows over the 16 chunk positions.
+//
+// K edge: rows k >= K of an m-contiguous operand lie outside its extent and
+// read as zeros.  For a k-contiguous operand the elements k >= K of the last,
+// partial k-tile hold whatever follows in memory (padding, possibly NaN), so
+// after that tile lands they are overwritten with zeros in LDS, for both
+// operands, before any wave reads it.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace mg {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+// Workgroup barrier without a memory fence: ordering of this workgroup's LDS
+// traffic is ensured by explicit waits; the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+__device__ __forceinline__ void wait_vmcnt_rt(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 32: wait_vmcnt<32>(); break;
+    case 40: wait_vmcnt<40>(); break;
+    case 48: wait_vmcnt<48>(); break;
+    default: wait_vmcnt<0>(); break;    // always safe
+    }
+}
+
+// One operand's k-tile in the LDS ring, loaded with direct-to-LDS buffer loads.
+template <int ROWS, int BK, int NWAVES, bool KMAJ>
+struct DmaOperand {
+    static constexpr int ES = 2, CE = 8;
+    static constexpr int BYTES = ROWS * BK * ES;
+    static constexpr int IPW = BYTES / 1024 / NWAVES;        // 1 KB loads per wave per tile
+    static_assert(BYTES % (1024 * NWAVES) == 0, "tile must split into 1 KB loads per wave");
+    // k-contiguous layout
+    static constexpr int CPR = BK / CE, RB = BK * ES;
+    // m-contiguous layout
+    static constexpr int RCH = ROWS * ES / 16, RBM = ROWS * ES;
+    static constexpr int MRPW = RCH >= 16 ? 1 : 16 / RCH;   // rows per bank window
+    static constexpr int MXR = (RCH >= 16 ? 16 : RCH) / 4;  // distinct 4-chunk offsets
+
+    int voff[IPW];
+
+    __device__ static __forceinline__ int mkey(int k) { return 4 * ((k / MRPW) % MXR); }
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
+    {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int slot = (wave * IPW + j) * 64 + lane;    // 16-byte LDS slot
+            if (KMAJ) {
+                const int row = slot / CPR, phys = slot % CPR;
+                const int c = swz_chunk<CPR, true>(row, phys);  // XOR is its own inverse
+                voff[j] = (int)(row * ld * ES) + c * 16;
+            } else {
+                const int k = slot / RCH, phys = slot % RCH;
+                const int c = phys ^ mkey(k);
+                voff[j] = (int)(k * ld * ES) + c * 16;
+            }
+        }
+    }
+
+    // Issue this wave's loads of the tile at (row0, k0) into `lds_tile`.
+    // The loads are written as inline assembly so that the compiler does not
+    // track their LDS writes: it would otherwise wait for all of them (vmcnt(0))
+    // before LDS reads it cannot prove independent, draining the ring.  The
+    // kernel orders them itself with wait_vmcnt and a barrier.
+    __device__ __forceinline__ void issue(const char* base, uint64_t bytes, int64_t ld, int row0,
+                                          int k0, char* lds_tile, int wave)
+    {
+        const int64_t origin = KMAJ ? ((int64_t)row0 * ld + k0) * ES : ((int64_t)k0 * ld + row0) * ES;
+        const uint64_t rem = (uint64_t)origin < bytes ? bytes - (uint64_t)origin : 0;
+        const uint64_t addr = (uint64_t)(base + origin);
+        i32x4 rs;   // buffer resource: base, stride 0, num_records, raw 32-bit format
+        rs[0] = (int)(uint32_t)addr;
+        rs[1] = (int)((uint32_t)(addr >> 32) & 0xffffu);
+        rs[2] = (int)(rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem);
+        rs[3] = kBufferFlags;
+        const uint32_t lds0 =
+            (uint32_t)(uintptr_t)(lds_char*)lds_tile + (uint32_t)(wave * IPW * 1024);
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024)), "v"(voff[j]),
+                           "s"(rs)
+                         : "memory", "m0");
+        }
+    }
+
+    // MFMA fragment: rows rbase .. rbase+MI-1 of the tile, k-group starting at kb.
+    template <int MI>
+    __device__ __forceinline__ i32x4 frag(const char* t, int rbase, int kb, int lane) const
+    {
+        if constexpr (KMAJ) {
+            const int row = rbase + lane % MI;
+            const int c = kb / CE + lane / MI;
+            return *(const i32x4*)(t + row * RB + swz_chunk<CPR, true>(row, c) * 16);
+        } else {
+            const int g = lane / 16, s = lane % 16;
+            int m, k;
+            if constexpr (MI == 32) {
+                m = rbase + 16 * (g % 2) + 4 * (s % 4);
+                k = kb + 8 * (g / 2) + s / 4;
+            } else {
+                m = rbase + 4 * (s % 4);
+                k = kb + 8 * g + s / 4;
+            }
+            const int k1 = k + 4;
+            const int c = m / 8, w = (m % 8) * 2;
+            const lds_char* p0 = (const lds_char*)(t + k * RBM + ((c ^ mkey(k)) * 16) + w);
+            const lds_char* p1 = (const lds_char*)(t + k1 * RBM + ((c ^ mkey(k1)) * 16) + w);
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+            i32x4 r;
+            r[0] = (int)(((uint32_t)(uint16_t)lo[0]) | ((uint32_t)(uint16_t)lo[1] << 16));
+            r[1] = (int)(((uint32_t)(uint16_t)lo[2]) | ((uint32_t)(uint16_t)lo[3] << 16));
+            r[2] = (int)(((uint32_t)(uint16_t)hi[0]) | ((uint32_t)(uint16_t)hi[1] << 16));
+            r[3] = (int)(((uint32_t)(uint16_t)hi[2]) | ((uint32_t)(uint16_t)hi[3] << 16));
+            return r;
+        }
+    }
+
+    // Zero the elements k >= kvalid of every row of a k-contiguous tile (the
+    // partial last k-tile), working with all NT threads of the workgroup.
+    template <int NT>
+    __device__ __forceinline__ void zero_tail(char* t, int kvalid, int tid) const
+    {
+        if constexpr (KMAJ) {
+            const int c0 = kvalid / CE;
+#pragma unroll 1
+            for (int idx = tid; idx < ROWS * CPR; idx += NT) {
+                const int row = idx / CPR, c = idx % CPR;
+                if (c < c0) continue;
+                i32x4* q = (i32x4*)(t + row * RB + swz_chunk<CPR, true>(row, c) * 16);
+                if (c * CE >= kvalid) {
+                    *q = i32x4{0, 0, 0, 0};
+                } else {
+                    i32x4 v = *q;
+                    *q = mask_k<In::F16>(v, c * CE, kvalid);   // 16-bit element mask
+                }
+            }
+        }
+    }
+};
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_dma_kernel(Params p)
+{
+    static_assert(TI != In::F32, "direct-to-LDS kernel is for 16-bit inputs");
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / MI, TN = WTN / MI;
+    constexpr int KG = MI == 32 ? 16 : 32;      // k per MFMA
+    constexpr int NG = BK / KG;                 // k-groups per tile
+    using OA = DmaOperand<BM, BK, NW, AK>;
+    using OB = DmaOperand<BN, BK, NW, BKM>;
+    constexpr int STAGE = OA::BYTES + OB::BYTES;
+    constexpr int LPT = OA::IPW + OB::IPW;      // loads per wave per tile
+    static_assert(BK % KG == 0, "BK must be a multiple of the MFMA k");
+    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
+    using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    OA oa;
+    OB ob;
+    oa.init(wave, lane, p.lda);
+    ob.init(wave, lane, p.ldb);
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
+
+    const int nkt = (p.K + BK - 1) / BK;
+    const int kvalid_last = p.K - (nkt - 1) * BK;
+    const bool ragged = kvalid_last != BK;
+
+    auto issue = [&](int t) {
+        char* st = smem + (t % STAGES) * STAGE;
+        oa.issue(p.A, p.a_bytes, p.lda, m0, t * BK, st, wave);
+        ob.issue(p.B, p.b_bytes, p.ldb, n0, t * BK, st + OA::BYTES, wave);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nkt) issue(s);
+
+    for (int t = 0; t < nkt; ++t) {
+        // Tile t has landed once at most min(STAGES-2, nkt-1-t) later tiles are outstanding.
+        const int later = min(STAGES - 2, nkt - 1 - t);
+        if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
+        else wait_vmcnt_rt(LPT * later);
+        char* st = smem + (t % STAGES) * STAGE;
+        if (t == nkt - 1 && ragged && (AK || BKM)) {
+            bare_barrier();
+            oa.template zero_tail<NT>(st, kvalid_last, tid);
+            ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
+        }
+        // A bare barrier: this wave's loads of tile t are complete (the vmcnt wait
+        // above), so after it every wave's part of tile t is in LDS.  A fenced
+        // __syncthreads() would also wait for the later tiles still in flight.
+        bare_barrier();
+        if (t + STAGES - 1 < nkt) issue(t + STAGES - 1);
+
+        const char* sa = st;
+        const char* sb = st + OA::BYTES;
+        i32x4 fa[2][TM], fb[2][TN];
+        auto read = [&](int g, int buf) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[buf][i] = oa.template frag<MI>(sa, wm * WTM + i * MI, g * KG, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[buf][j] = ob.template frag<MI>(sb, wn * WTN + j * MI, g * KG, lane);
+        };
+        read(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 < NG) read(g + 1, (g + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) mfma_step<TI, MI>(fa[g & 1][i], fb[g & 1][j], acc[i][j]);
+            if (g + 1 < NG) interleave<TM * TN, (AK ? 1 : 2) * TM + (BKM ? 1 : 2) * TN, 0, 0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue (as in gemm_kernel): fp32 accumulators -> output type, predicated stores.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * WTN + j * MI + (lane % MI);
+            const int mb = m0 + wm * WTM + i * MI;
+            if constexpr (MI == 32) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = mb + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mb + (lane / 16) * 4 + r;
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES>
+struct DmaInst {
+    template <bool AK, bool BKM>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        Params copy = p;
+        void* args[] = {&copy};
+        return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM>,
+                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+    }
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        switch (layout) {
+        case 0: return go<true, true>(p, s);
+        case 1: return go<true, false>(p, s);
+        case 2: return go<false, true>(p, s);
+        default: return go<false, false>(p, s);
+        }
+    }
+};
+
+}  // namespace mg

@@ -7,7 +7,7 @@ namespace mg {
 #define MG_ENTRY(BM, BN, BK, WM, WN, MI, SWZ)                                        \
     {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2" MG_SWZNAME_##SWZ, \
      BM, BN, BK, WM, WN, MI, SWZ,                                                  \
-     &Inst<In::F32, Out::F32, BM, BN, BK, WM, WN, MI, SWZ>::launch},
+     &Inst<In::F32, Out::F32, BM, BN, BK, WM, WN, MI, SWZ>::launch, 2, false},
 
 static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY)};
 

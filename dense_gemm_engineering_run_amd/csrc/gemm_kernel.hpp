@@ -21,8 +21,8 @@
 //    loop serves all four layouts.
 //  * LDS: a ring of STAGES (2) buffers of [BM][BK] + [BN][BK]; 16-byte chunks
 //    are XOR-swizzled by row so that the 128-bit writes and the 128-bit
-//    fragment reads of a quarter-wave hit distinct banks (the SGEMM example
-//    pads rows for the same purpose).
+//    fragment reads of a quarter-wave hit distinct banks of gfx950's 256-byte
+//    bank window (the SGEMM example pads rows for the same purpose).
 //  * Registers: the global loads of tile t+2 are issued while tile t is
 //    consumed and land in VGPRs that are written to LDS after the MFMAs of
 //    tile t+1's predecessor finish (one tile in flight per operand); the MFMA
@@ -86,16 +86,25 @@ __device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// LDS bank window of gfx950: 64 banks x 4 bytes = 256 bytes = 16 chunks of
+// 16 B (measured: 128-bit reads of 16 lanes from 16 distinct chunk positions of
+// a 256-byte window complete without conflict; 8 positions in 128 bytes do not).
+constexpr int kBankWindowChunks = 16;
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row` (rows of CPR
+// chunks).  Rows shorter than the bank window share it; the XOR term gives the
+// rows that share a window position different chunks, so that the 16 lanes of a
+// quarter-wave reading the same logical chunk of 16 consecutive rows (MFMA
+// fragment reads) and the lanes writing consecutive chunks of a row both hit 16
+// distinct positions.
 template <int CPR, bool SWZ>
 __device__ __forceinline__ int swz_chunk(int row, int c)
 {
     if constexpr (!SWZ) {
         return c;
     } else {
-        // 128-byte bank window = 8 chunks of 16 B.  Rows shorter than the
-        // window share it; the XOR term walks over the chunks of the window.
-        constexpr int RPW = CPR >= 8 ? 1 : 8 / CPR;   // rows per window
-        constexpr int XM = CPR >= 8 ? 8 : CPR;        // xor range
+        constexpr int RPW = CPR >= kBankWindowChunks ? 1 : kBankWindowChunks / CPR;
+        constexpr int XM = CPR >= kBankWindowChunks ? kBankWindowChunks : CPR;
         return c ^ ((row / RPW) % XM);
     }
 }
@@ -288,132 +297,214 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn)
     tn = r / gsz;
 }
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_kernel(Params p)
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+
+// Interleave NR LDS reads, NW LDS writes and NL global loads among NM MFMAs
+// of one scheduling region: after each MFMA, the next share of each class.
+template <int NM, int NR, int NW, int NL>
+__device__ __forceinline__ void interleave()
 {
-    constexpr int NT = WM * WN * 64;
-    constexpr int ES = TI == In::F32 ? 4 : 2;
-    constexpr int CE = 16 / ES;
-    constexpr int CPR = BK / CE;
-    constexpr int RB = BK * ES;
-    constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
-    constexpr int TM = WTM / MI, TN = WTN / MI;      // MFMA tiles per wave
-    constexpr int NQ = 64 / MI;                      // lane groups along k
-    constexpr int NG = CPR / NQ;                     // k-groups per BK
-    constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int PR = (NR + NM - 1) / NM, PW = (NW + NM - 1) / NM, PL = (NL + NM - 1) / NM;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (PR > 0 && i * PR < NR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PR, 0);
+        if (PW > 0 && i * PW < NW) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, PW, 0);
+        if (PL > 0 && i * PL < NL) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, PL, 0);
+    }
+}
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
+struct GemmTile {
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int ES = TI == In::F32 ? 4 : 2;
+    static constexpr int CE = 16 / ES;
+    static constexpr int CPR = BK / CE;
+    static constexpr int RB = BK * ES;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+    static constexpr int TM = WTM / MI, TN = WTN / MI;   // MFMA tiles per wave
+    static constexpr int NQ = 64 / MI;                   // lane groups along k
+    static constexpr int NG = CPR / NQ;                  // k-groups per BK
+    static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int MF_PER = TI == In::F32 ? 4 : 1; // MFMAs per fragment pair
+    static constexpr int NMF = TM * TN * MF_PER;         // MFMAs per k-group
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert(CPR % NQ == 0, "BK too small for this MFMA shape");
     static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
     using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+    using LA = TileLoader<TI, BM, BK, NT, AK, SWZ>;
+    using LB = TileLoader<TI, BN, BK, NT, BKM, SWZ>;
+    static constexpr int NW = (AK ? LA::PER : LA::PER * CE) + (BKM ? LB::PER : LB::PER * CE);
+    static constexpr int NL = LA::REGS + LB::REGS;
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    LA la;
+    LB lb;
+    Acc acc[TM][TN];
+    i32x4 fa[2][TM], fb[2][TN];
+    int wm, wn, frow, fq, tid;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    __device__ __forceinline__ void read_frags(const char* sa, int g, int buf)
+    {
+        const char* sb = sa + A_BYTES;
+        const int c = g * NQ + fq;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * MI + frow;
+            fa[buf][i] = *(const i32x4*)(sa + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int row = wn * WTN + j * MI + frow;
+            fb[buf][j] = *(const i32x4*)(sb + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
+        }
+    }
+
+    __device__ __forceinline__ void mma(int buf)
+    {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                mfma_step<TI, MI>(fa[buf][i], fb[buf][j], acc[i][j]);
+    }
+
+    // One k-tile: MFMAs on LDS stage `cur` (whose group-0 fragments are already
+    // in fa/fb[0]).  WRITE: the staged registers (tile t+1) go to the other
+    // stage during group 0; LOAD: tile t+2 is fetched into the registers during
+    // group 1 (group 0 when there is only one).  NEXT: after a barrier, the
+    // group-0 fragments of the other stage are read for the next tile.
+    template <bool WRITE, bool LOAD, bool NEXT>
+    __device__ __forceinline__ void tile(char* smem, int cur, const Params& p, int m0, int n0,
+                                         int k_load)
+    {
+        char* sa = smem + cur * STAGE;
+        char* nxt = smem + (cur ^ 1) * STAGE;
+        constexpr int LOAD_G = NG > 1 ? 1 : 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            // Fence: nothing moves between k-groups, so the reads issued here
+            // for group g+1 are consumed only after this group's MFMAs.
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 < NG) read_frags(sa, g + 1, (g + 1) & 1);
+            if (WRITE && g == 0) {
+                la.store(nxt, tid);
+                lb.store(nxt + A_BYTES, tid);
+            }
+            if (LOAD && g == LOAD_G) {
+                la.load(p.A, p.a_bytes, p.lda, m0, k_load, tid);
+                lb.load(p.B, p.b_bytes, p.ldb, n0, k_load, tid);
+            }
+            mma(g & 1);
+            if (g + 1 < NG) {
+                if (WRITE && g == 0 && LOAD && g == LOAD_G)
+                    interleave<NMF, TM + TN, NW, NL>();
+                else if (WRITE && g == 0)
+                    interleave<NMF, TM + TN, NW, 0>();
+                else if (LOAD && g == LOAD_G)
+                    interleave<NMF, TM + TN, 0, NL>();
+                else
+                    interleave<NMF, TM + TN, 0, 0>();
+            } else {
+                if (WRITE && g == 0 && LOAD && g == LOAD_G)
+                    interleave<NMF, 0, NW, NL>();
+                else if (WRITE && g == 0)
+                    interleave<NMF, 0, NW, 0>();
+                else if (LOAD && g == LOAD_G)
+                    interleave<NMF, 0, 0, NL>();
+                else
+                    interleave<NMF, 0, 0, 0>();
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NEXT) {
+            __syncthreads();
+            read_frags(nxt, 0, 0);
+        }
+    }
+};
+
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_kernel(Params p)
+{
+    using T = GemmTile<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>;
+    __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+
+    T t;
+    t.tid = threadIdx.x;
+    const int lane = t.tid & 63;
+    const int wave = t.tid >> 6;
+    t.wm = wave / WN;
+    t.wn = wave % WN;
+    t.frow = lane % MI;
+    t.fq = lane / MI;
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    TileLoader<TI, BM, BK, NT, AK, SWZ> la;
-    TileLoader<TI, BN, BK, NT, BKM, SWZ> lb;
-    la.init(tid, p.lda);
-    lb.init(tid, p.ldb);
-
-    Acc acc[TM][TN];
+    t.la.init(t.tid, p.lda);
+    t.lb.init(t.tid, p.ldb);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = Acc{};
+        for (int j = 0; j < T::TN; ++j)
+            t.acc[i][j] = typename T::Acc{};
 
     const int nkt = (p.K + BK - 1) / BK;
     const bool ragged = (p.K % BK) != 0;
 
-    // Fragment read: row r of the wave's operand sub-tile, k-group g.
-    const int frow = lane % MI;
-    const int fq = lane / MI;
-
     if (nkt > 0) {
-        la.load(p.A, p.a_bytes, p.lda, m0, 0, tid);
-        lb.load(p.B, p.b_bytes, p.ldb, n0, 0, tid);
-        if (nkt == 1 && ragged) { la.mask(0, p.K, tid); lb.mask(0, p.K, tid); }
-        la.store(smem, tid);
-        lb.store(smem + A_BYTES, tid);
+        // Prologue: tile 0 -> LDS stage 0, tile 1 -> registers, group-0 fragments.
+        t.la.load(p.A, p.a_bytes, p.lda, m0, 0, t.tid);
+        t.lb.load(p.B, p.b_bytes, p.ldb, n0, 0, t.tid);
+        if (nkt == 1 && ragged) { t.la.mask(0, p.K, t.tid); t.lb.mask(0, p.K, t.tid); }
+        t.la.store(smem, t.tid);
+        t.lb.store(smem + T::A_BYTES, t.tid);
         if (nkt > 1) {
-            la.load(p.A, p.a_bytes, p.lda, m0, BK, tid);
-            lb.load(p.B, p.b_bytes, p.ldb, n0, BK, tid);
+            t.la.load(p.A, p.a_bytes, p.lda, m0, BK, t.tid);
+            t.lb.load(p.B, p.b_bytes, p.ldb, n0, BK, t.tid);
         }
         __syncthreads();
-    }
+        t.read_frags(smem, 0, 0);
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const char* sa = smem + (kt & 1) * STAGE;
-        const char* sb = sa + A_BYTES;
-
-        i32x4 fa[2][TM], fb[2][TN];
-        auto read_frags = [&](int g, int buf) {
-            const int c = g * NQ + fq;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                int row = wm * WTM + i * MI + frow;
-                fa[buf][i] = *(const i32x4*)(sa + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                int row = wn * WTN + j * MI + frow;
-                fb[buf][j] = *(const i32x4*)(sb + row * RB + swz_chunk<CPR, SWZ>(row, c) * 16);
-            }
-        };
-        read_frags(0, 0);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            if (g + 1 < NG) read_frags(g + 1, (g + 1) & 1);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    mfma_step<TI, MI>(fa[g & 1][i], fb[g & 1][j], acc[i][j]);
-        }
-
+        // Steady state: every iteration writes tile kt+1 and loads tile kt+2.
+        int kt = 0;
+        for (; kt + 2 < nkt; ++kt)
+            t.template tile<true, true, true>(smem, kt & 1, p, m0, n0, (kt + 2) * BK);
+        // Tail: tile nkt-2 writes the (possibly ragged) last tile, then the last tile.
         if (kt + 1 < nkt) {
-            if (kt + 1 == nkt - 1 && ragged) {
-                la.mask((kt + 1) * BK, p.K, tid);
-                lb.mask((kt + 1) * BK, p.K, tid);
-            }
-            char* nxt = smem + ((kt + 1) & 1) * STAGE;
-            la.store(nxt, tid);
-            lb.store(nxt + A_BYTES, tid);
-            if (kt + 2 < nkt) {
-                la.load(p.A, p.a_bytes, p.lda, m0, (kt + 2) * BK, tid);
-                lb.load(p.B, p.b_bytes, p.ldb, n0, (kt + 2) * BK, tid);
-            }
+            if (ragged) { t.la.mask((kt + 1) * BK, p.K, t.tid); t.lb.mask((kt + 1) * BK, p.K, t.tid); }
+            t.template tile<true, false, true>(smem, kt & 1, p, m0, n0, 0);
+            ++kt;
         }
-        __syncthreads();
+        t.template tile<false, false, false>(smem, kt & 1, p, m0, n0, 0);
     }
 
     // Epilogue: fp32 accumulators -> output type, predicated stores.
+    constexpr int MI_ = MI;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WTN + j * MI + (lane % MI);
-            const int mb = m0 + wm * WTM + i * MI;
-            if constexpr (MI == 32) {
+        for (int j = 0; j < T::TN; ++j) {
+            const int n = n0 + t.wn * T::WTN + j * MI_ + (lane % MI_);
+            const int mb = m0 + t.wm * T::WTM + i * MI_;
+            if constexpr (MI_ == 32) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = mb + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
-                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, t.acc[i][j][r]);
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = mb + (lane / 16) * 4 + r;
-                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, t.acc[i][j][r]);
                 }
             }
         }
@@ -428,6 +519,8 @@ struct KernelEntry {
     int BM, BN, BK, WM, WN, MI;
     bool swz;
     LaunchFn launch;
+    int stages;        // LDS ring depth
+    bool dma;          // direct HBM -> LDS loads (16-bit inputs)
 };
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>

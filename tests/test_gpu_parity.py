@@ -132,13 +132,14 @@ def test_every_config_every_layout(dtype):
     code = gi.DTYPE_CODE[dtype]
     for cfg in range(g.gemm_num_configs(code)):
         name = g.gemm_config_describe(code, cfg)
-        for am, bm, cm in LAYOUTS8:
-            prob = gi.problem(300, 200, 136, am, bm, cm, dtype, "int5", seed=cfg)
+        for (M, N, K), (am, bm, cm) in itertools.product([(300, 200, 136), (97, 65, 37)], LAYOUTS8):
+            prob = gi.problem(M, N, K, am, bm, cm, dtype, "int5", seed=cfg, pad_fill=float("nan"))
             c, flat, st = gu.run(prob, config=cfg)
             assert st == 0
             assert g.gemm_last_config() == cfg
             ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
-            assert ok, (name, am, bm, cm, info)
+            assert ok, (name, M, N, K, am, bm, cm, info)
+            assert gu.padding_intact(flat, prob)
         log(f"{name}: 8 layouts exact")
 
 

@@ -1,0 +1,69 @@
+"""The offline tuner's search, resume and table logic against a scripted fake
+backend (no GPU): the fastest passing candidate wins, failing / mislaunched /
+crashing candidates are dropped, a rerun resumes from the log, and the table
+it writes is one the library loads."""
+import json
+
+import dense_gemm_engineering_run_amd as g
+from dense_gemm_engineering_run_amd import tune as T
+
+
+def names(dtype):
+    return [g.gemm_config_describe(dtype, i) for i in range(g.gemm_num_configs(dtype))]
+
+
+def scripted(script, calls):
+    def measure(key, cid):
+        calls.append((key, cid))
+        r = script[cid]
+        if r == "raise":
+            raise RuntimeError("launch failed")
+        t, ok, launched = r
+        return dict(launched=launched, error=None, median_us=t, mean_us=t, **{"pass": ok})
+    return measure
+
+
+def test_fastest_passing_candidate_wins_and_failures_are_dropped(tmp_path):
+    key = (0, "k", "k", "n", 1000, 1000, 1000)
+    n = g.gemm_num_configs(0)
+    script = {i: (100.0 + i, True, i) for i in range(n)}
+    script[1] = (5.0, True, 1)        # the winner
+    script[2] = (3.0, False, 2)       # faster but wrong result
+    script[3] = "raise"               # crashes
+    script[4] = (1.0, True, 0)        # reports a different config than requested
+    calls = []
+    log = tmp_path / "log.jsonl"
+    table = tmp_path / "table.txt"
+    best = T.tune([key], scripted(script, calls), names, str(log), str(table), verbose=False)
+    assert best[T.key_str(key)]["config"] == 1
+    recs = [json.loads(l) for l in open(log)]
+    assert len(recs) == n
+    by = {r["config"]: r for r in recs}
+    assert not by[2]["pass"] and not by[3]["pass"] and not by[4]["pass"]
+    assert "instead of" in by[4]["error"]
+    # resume: nothing is measured again
+    calls.clear()
+    with open(log, "a") as f:
+        f.write('{"torn": ')      # an interrupted write
+    best2 = T.tune([key], scripted(script, calls), names, str(log), str(table), verbose=False)
+    assert calls == [] and best2[T.key_str(key)]["config"] == 1
+    # the library reads the table and selects the tuned config
+    saved = g.gemm_tuning_size()
+    try:
+        assert g.gemm_load_tuning(str(table)) == 0
+        assert g.gemm_select_config(1000, 1000, 1000, "k", "k", "n", 0) == 1
+    finally:
+        from dense_gemm_engineering_run_amd import _binding as b
+        import os
+        g.gemm_load_tuning(b.DEFAULT_TABLE if os.path.exists(b.DEFAULT_TABLE) else None)
+    assert g.gemm_tuning_size() == saved
+
+
+def test_no_passing_candidate_leaves_key_untuned(tmp_path):
+    key = (1, "m", "n", "m", 64, 64, 64)
+    n = g.gemm_num_configs(1)
+    script = {i: (1.0, False, i) for i in range(n)}
+    best = T.tune([key], scripted(script, []), names, None, str(tmp_path / "t.txt"),
+                  verbose=False)
+    assert best == {}
+    assert [l for l in open(tmp_path / "t.txt") if not l.startswith("#")] == []
