@@ -126,11 +126,22 @@ class Problem:
         if st != 0:
             raise RuntimeError(g.gemm_status_str(st))
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, min_warm_s=0.0):
+        """Mean ms per launch over `steps` launches, after `warmup` untimed
+        launches and, with min_warm_s, enough further launches to keep the GPU
+        busy that long first (clocks ramp up over tens of ms after idle)."""
         import torch
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
+        if min_warm_s > 0:
+            t0 = time.perf_counter()
+            n = 1
+            while time.perf_counter() - t0 < min_warm_s:
+                for _ in range(n):
+                    self.launch()
+                torch.cuda.synchronize()
+                n *= 2
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(self.stream)
@@ -171,10 +182,16 @@ def cpu_baseline(prob, target_s):
                               p["B"], p["ldb"], rows=(0, rows), threads=threads)
         return ref, time.perf_counter() - t
 
-    _, t_probe = run(min(M, 2 * threads))
-    rows = int(min(M, max(threads, 2 * threads * target_s / max(t_probe, 1e-3))))
-    rows = max(threads, rows // threads * threads)
+    # Size the sample: a probe run, then rescale once more if the first sized
+    # run is still well short of the target (the repack of B is a fixed cost).
+    rows = min(M, 2 * threads)
     ref, t = run(rows)
+    for _ in range(2):
+        if t >= 0.6 * target_s or rows >= M:
+            break
+        rows = int(min(M, max(threads, rows * target_s / max(t, 1e-3))))
+        rows = max(min(threads, M), rows // threads * threads)
+        ref, t = run(rows)
     flat = prob.c.cpu().numpy()
     if p["out_type"] != "f32":
         flat = flat.view(np.uint16)
@@ -277,7 +294,7 @@ def main():
         for w in others:
             print(f"bench: {w}", file=sys.stderr, flush=True)
             pr = Problem(w)
-            record["workloads"][w] = pr.summary(pr.time(args.other_steps, args.warmup))
+            record["workloads"][w] = pr.summary(pr.time(args.other_steps, args.warmup, 0.3))
             del pr
             torch.cuda.empty_cache()
 

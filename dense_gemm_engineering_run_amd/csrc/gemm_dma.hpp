@@ -130,7 +130,7 @@ struct DmaOperand {
     // before LDS reads it cannot prove independent, draining the ring.  The
     // kernel orders them itself with wait_vmcnt and a barrier.
     __device__ __forceinline__ void issue(const char* base, uint64_t bytes, int64_t ld, int row0,
-                                          int k0, char* lds_tile, int wave)
+                                          int k0, char* lds_tile, int wave, int j0 = 0, int j1 = IPW)
     {
         const int64_t origin = KMAJ ? ((int64_t)row0 * ld + k0) * ES : ((int64_t)k0 * ld + row0) * ES;
         const uint64_t rem = (uint64_t)origin < bytes ? bytes - (uint64_t)origin : 0;
@@ -144,6 +144,7 @@ struct DmaOperand {
             (uint32_t)(uintptr_t)(lds_char*)lds_tile + (uint32_t)(wave * IPW * 1024);
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
+            if (j < j0 || j >= j1) continue;
             asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :
                          : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024)), "v"(voff[j]),
@@ -276,7 +277,9 @@ gemm_dma_kernel(Params p)
         // above), so after it every wave's part of tile t is in LDS.  A fenced
         // __syncthreads() would also wait for the later tiles still in flight.
         bare_barrier();
-        if (t + STAGES - 1 < nkt) issue(t + STAGES - 1);
+        const bool more = t + STAGES - 1 < nkt;
+        char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
+        const int nk0 = (t + STAGES - 1) * BK;
 
         const char* sa = st;
         const char* sb = st + OA::BYTES;
@@ -291,6 +294,13 @@ gemm_dma_kernel(Params p)
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             __builtin_amdgcn_sched_barrier(0);
+            // This k-group's share of the loads of tile t+STAGES-1 (into the stage
+            // tile t-1 used, which every wave has left at the barrier above).
+            if (more) {
+                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
+                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
+                         (g + 1) * OB::IPW / NG);
+            }
             if (g + 1 < NG) read(g + 1, (g + 1) & 1);
 #pragma unroll
             for (int i = 0; i < TM; ++i)

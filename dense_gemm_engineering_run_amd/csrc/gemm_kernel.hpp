@@ -269,6 +269,18 @@ __device__ __forceinline__ void mfma_step(const i32x4& a, const i32x4& b, f32x4&
     }
 }
 
+// One fp32 MFMA (k = 2 for 32x32, k = 4 for 16x16) on raw 32-bit operands.
+template <int MI>
+__device__ __forceinline__ void mfma_f32_one(int a, int b, f32x16& acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a), __int_as_float(b), acc, 0, 0, 0);
+}
+template <int MI>
+__device__ __forceinline__ void mfma_f32_one(int a, int b, f32x4& acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a), __int_as_float(b), acc, 0, 0, 0);
+}
+
 template <Out TO>
 __device__ __forceinline__ void store_out(char* C, int64_t idx, float v)
 {
@@ -366,11 +378,23 @@ struct GemmTile {
 
     __device__ __forceinline__ void mma(int buf)
     {
+        if constexpr (TI == In::F32) {
+            // The 4 k values of a fragment feed 4 MFMAs on one accumulator;
+            // walk the accumulators innermost so consecutive MFMAs are independent.
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                mfma_step<TI, MI>(fa[buf][i], fb[buf][j], acc[i][j]);
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        mfma_f32_one<MI>(fa[buf][i][e], fb[buf][j][e], acc[i][j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    mfma_step<TI, MI>(fa[buf][i], fb[buf][j], acc[i][j]);
+        }
     }
 
     // One k-tile: MFMAs on LDS stage `cur` (whose group-0 fragments are already
