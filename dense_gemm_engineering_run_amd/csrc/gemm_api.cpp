@@ -220,15 +220,16 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K)
         int id = find_config(dtype, name);
         return id < 0 ? 0 : id;
     };
+    // Large problems (at least a full wave of 256x256 tiles) go to the
+    // direct-to-LDS kernels; smaller ones to tiles that still fill the 256 CUs.
     const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0);
     if (dtype == GEMM_DTYPE_F32) {
-        if (tiles256 >= 512) return pick("256x256x16 w2x2 mfma32 s2 swz");
-        if (tiles256 >= 128) return pick("256x128x16 w2x2 mfma32 s2 swz");
-        if (M * N >= 512 * 512) return pick("128x128x16 w2x2 mfma32 s2 swz");
+        if (tiles256 >= 256) return pick("256x256x32 w2x2 mfma32 s2 dma");
+        if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 swz");
         return pick("64x64x16 w2x2 mfma16 s2 swz");
     }
-    if (tiles256 >= 256) return pick("256x256x64 w2x2 mfma32 s2 swz");
-    if (tiles256 >= 64) return pick("256x128x64 w2x2 mfma32 s2 swz");
+    if (tiles256 >= 192) return pick("256x256x64 w2x2 mfma32 s2 dma");
+    if (tiles256 >= 64) return pick("128x128x64 w2x2 mfma32 s4 dma");
     if (M * N >= 512 * 512) return pick("128x128x64 w2x2 mfma32 s2 swz");
     return pick("64x64x64 w2x2 mfma16 s2 swz");
 }

@@ -1,5 +1,5 @@
 // Kernel instantiations for dtype f32 (inputs F32, output F32).
-#include "gemm_kernel.hpp"
+#include "gemm_f32dma.hpp"
 #include "configs.def"
 
 namespace mg {
@@ -9,7 +9,11 @@ namespace mg {
      BM, BN, BK, WM, WN, MI, SWZ,                                                  \
      &Inst<In::F32, Out::F32, BM, BN, BK, WM, WN, MI, SWZ>::launch, 2, false},
 
-static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY)};
+#define MG_F32DMA_ENTRY(BM, BN, BK, WM, WN, ST)                                      \
+    {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma",               \
+     BM, BN, BK, WM, WN, 32, true, &F32DmaInst<Out::F32, BM, BN, BK, WM, WN, ST>::launch, ST, true},
+
+static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIGS(MG_F32DMA_ENTRY)};
 
 const KernelEntry* entries_f32(int* n)
 {

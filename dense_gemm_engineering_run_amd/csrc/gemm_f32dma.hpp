@@ -1,0 +1,322 @@
+// gemm_f32dma.hpp -- gfx950 fp32 GEMM with direct HBM -> LDS loads.
+//
+// Same operation and canonical form as gemm_kernel.hpp (C = A * B^T, C
+// n-major; CuTe DSL Ampere SGEMM example, module docstring), for fp32 inputs on
+// v_mfma_f32_32x32x2_f32.  Operands go from HBM straight into a ring of LDS
+// stages with buffer_load_dwordx4 ... lds (as in gemm_dma.hpp), in their own
+// layout: k-contiguous operands as [rows][BK], m/n-contiguous operands as
+// [BK][rows].  No operand is transposed anywhere; instead each 128-bit LDS
+// read feeds four MFMAs:
+//
+//  * k-contiguous operand: a lane reads 4 consecutive k of its row; MFMA e
+//    (e = 0..3) takes element e.  Lane half h = lane/32 supplies k = 4h + e of
+//    an 8-k step, the same relabelling for A and B, so each output element's
+//    sum is unchanged up to rounding order.
+//  * m-contiguous operand: for each e, a lane reads 4 consecutive m at
+//    k = 4h + e; element v is row 4q + v of a 128-row block (q = lane mod 32),
+//    i.e. the MFMA's 32 rows are 4 interleaved row sets v = 0..3.  The
+//    epilogue undoes the interleave.  (The SGEMM example permutes its thread
+//    layout along m and n for vectorised shared-memory reads in the same way.)
+//
+// Per 8-k step and per 128 rows (or columns) an operand needs 4 LDS reads of
+// 128 bits in either layout; a 128x128 wave tile issues 64 MFMAs per step.
+// When both A and B are m/n-contiguous, a lane's 16 accumulators hold 4x4
+// blocks of C, written with 128-bit stores.
+#pragma once
+
+#include "gemm_dma.hpp"
+
+namespace mg {
+
+// One fp32 operand's k-tile in the LDS ring.
+template <int ROWS, int BK, int NWAVES, bool KMAJ>
+struct F32Operand {
+    static constexpr int ES = 4, CE = 4;
+    static constexpr int BYTES = ROWS * BK * ES;
+    static constexpr int IPW = BYTES / 1024 / NWAVES;
+    static_assert(BYTES % (1024 * NWAVES) == 0, "tile must split into 1 KB loads per wave");
+    static constexpr int CPR = BK / CE, RB = BK * ES;       // k-contiguous layout
+    static constexpr int RCH = ROWS / CE, RBM = ROWS * ES;  // m-contiguous layout (no swizzle:
+                                                            // its reads are contiguous)
+    int voff[IPW];
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
+    {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int slot = (wave * IPW + j) * 64 + lane;
+            if (KMAJ) {
+                const int row = slot / CPR, phys = slot % CPR;
+                voff[j] = (int)(row * ld * ES) + swz_chunk<CPR, true>(row, phys) * 16;
+            } else {
+                const int k = slot / RCH, c = slot % RCH;
+                voff[j] = (int)(k * ld * ES) + c * 16;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void issue(const char* base, uint64_t bytes, int64_t ld, int row0,
+                                          int k0, char* lds_tile, int wave, int j0 = 0, int j1 = IPW)
+    {
+        const int64_t origin = KMAJ ? ((int64_t)row0 * ld + k0) * ES : ((int64_t)k0 * ld + row0) * ES;
+        const uint64_t rem = (uint64_t)origin < bytes ? bytes - (uint64_t)origin : 0;
+        const uint64_t addr = (uint64_t)(base + origin);
+        i32x4 rs;
+        rs[0] = (int)(uint32_t)addr;
+        rs[1] = (int)((uint32_t)(addr >> 32) & 0xffffu);
+        rs[2] = (int)(rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem);
+        rs[3] = kBufferFlags;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds_tile + (uint32_t)(wave * IPW * 1024);
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            if (j < j0 || j >= j1) continue;
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024)), "v"(voff[j]), "s"(rs)
+                         : "memory", "m0");
+        }
+    }
+
+    // k-contiguous: 4 consecutive k (4h .. 4h+3 of the 8-k step at kb) of row rbase + lane%32.
+    __device__ __forceinline__ i32x4 frag_k(const char* t, int rbase, int kb, int lane) const
+    {
+        const int row = rbase + lane % 32;
+        const int c = kb / CE + lane / 32;
+        return *(const i32x4*)(t + row * RB + swz_chunk<CPR, true>(row, c) * 16);
+    }
+
+    // m-contiguous: rows cbase + 4q .. 4q+3 (q = lane%32) at k = kb + 4h + e.
+    __device__ __forceinline__ i32x4 frag_m(const char* t, int cbase, int kb, int e, int lane) const
+    {
+        const int k = kb + 4 * (lane / 32) + e;
+        return *(const i32x4*)(t + k * RBM + (cbase + 4 * (lane % 32)) * ES);
+    }
+
+    template <int NT>
+    __device__ __forceinline__ void zero_tail(char* t, int kvalid, int tid) const
+    {
+        if constexpr (KMAJ) {
+            const int c0 = kvalid / CE;
+#pragma unroll 1
+            for (int idx = tid; idx < ROWS * CPR; idx += NT) {
+                const int row = idx / CPR, c = idx % CPR;
+                if (c < c0) continue;
+                i32x4* q = (i32x4*)(t + row * RB + swz_chunk<CPR, true>(row, c) * 16);
+                if (c * CE >= kvalid) *q = i32x4{0, 0, 0, 0};
+                else *q = mask_k<In::F32>(*q, c * CE, kvalid);
+            }
+        }
+    }
+};
+
+// Units of an operand within a wave tile: k-contiguous -> WT/32 row blocks of
+// 32 rows; m-contiguous -> WT/128 blocks of 128 rows x 4 row variants.
+template <bool KMAJ, int WT>
+struct Units {
+    static_assert(KMAJ ? WT % 32 == 0 : WT % 128 == 0, "wave tile size for this layout");
+    static constexpr int N = WT / 32;
+    // global row (relative to the wave tile) of MFMA row index r in unit u
+    __device__ static __forceinline__ int row(int u, int r) { return KMAJ ? u * 32 + r : (u / 4) * 128 + 4 * r + (u % 4); }
+};
+
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_f32dma_kernel(Params p)
+{
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    using UA = Units<AK, WTM>;
+    using UB = Units<BKM, WTN>;
+    constexpr int NA = UA::N, NB = UB::N;
+    constexpr int NG = BK / 8;                  // 8-k steps per tile
+    using OA = F32Operand<BM, BK, NW, AK>;
+    using OB = F32Operand<BN, BK, NW, BKM>;
+    constexpr int STAGE = OA::BYTES + OB::BYTES;
+    constexpr int LPT = OA::IPW + OB::IPW;
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    OA oa;
+    OB ob;
+    oa.init(wave, lane, p.lda);
+    ob.init(wave, lane, p.ldb);
+
+    f32x16 acc[NA][NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+    const int nkt = (p.K + BK - 1) / BK;
+    const int kvalid_last = p.K - (nkt - 1) * BK;
+    const bool ragged = kvalid_last != BK;
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+        if (s < nkt) {
+            char* st = smem + s * STAGE;
+            oa.issue(p.A, p.a_bytes, p.lda, m0, s * BK, st, wave);
+            ob.issue(p.B, p.b_bytes, p.ldb, n0, s * BK, st + OA::BYTES, wave);
+        }
+    }
+
+    for (int t = 0; t < nkt; ++t) {
+        const int later = min(STAGES - 2, nkt - 1 - t);
+        if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
+        else wait_vmcnt_rt(LPT * later);
+        char* st = smem + (t % STAGES) * STAGE;
+        if (t == nkt - 1 && ragged && (AK || BKM)) {
+            bare_barrier();
+            oa.template zero_tail<NT>(st, kvalid_last, tid);
+            ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+        bare_barrier();
+        const bool more = t + STAGES - 1 < nkt;
+        char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
+        const int nk0 = (t + STAGES - 1) * BK;
+        const char* sa = st;
+        const char* sb = st + OA::BYTES;
+
+        // Fragments of one 8-k step: va[buf][e][u] is the A value of unit u for
+        // k sub-index e; the next step's fragments are read during this step.
+        int va[2][4][NA], vb[2][4][NB];
+        auto read = [&](int g, int buf) {
+            const int kb = g * 8;
+            if constexpr (AK) {
+#pragma unroll
+                for (int u = 0; u < NA; ++u) {
+                    const i32x4 f = oa.frag_k(sa, wm * WTM + u * 32, kb, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) va[buf][e][u] = f[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int cb = 0; cb < NA / 4; ++cb) {
+                        const i32x4 f = oa.frag_m(sa, wm * WTM + cb * 128, kb, e, lane);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) va[buf][e][cb * 4 + v] = f[v];
+                    }
+            }
+            if constexpr (BKM) {
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const i32x4 f = ob.frag_k(sb, wn * WTN + u * 32, kb, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vb[buf][e][u] = f[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int cb = 0; cb < NB / 4; ++cb) {
+                        const i32x4 f = ob.frag_m(sb, wn * WTN + cb * 128, kb, e, lane);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) vb[buf][e][cb * 4 + v] = f[v];
+                    }
+            }
+        };
+        constexpr int RA = AK ? NA : NA, RB_ = BKM ? NB : NB;   // 128-bit reads per step
+        read(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) {
+                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
+                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
+                         (g + 1) * OB::IPW / NG);
+            }
+            if (g + 1 < NG) read(g + 1, (g + 1) & 1);
+            const int b = g & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < NA; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(va[b][e][i]),
+                                                                          __int_as_float(vb[b][e][j]), acc[i][j], 0, 0, 0);
+            if (g + 1 < NG) interleave<4 * NA * NB, RA + RB_, 0, 0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue.  D row r of unit u maps to tile row UA::row(u, r); likewise columns.
+    const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
+    if constexpr (!AK && !BKM && TO == Out::F32) {
+        // Both interleaved: for register index i a lane holds rows 4r .. 4r+3 of
+        // each 128-row block and columns 4c .. 4c+3 -> 128-bit row stores.
+#pragma unroll
+        for (int ca = 0; ca < NA / 4; ++ca)
+#pragma unroll
+            for (int cbk = 0; cbk < NB / 4; ++cbk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+                    const int c = lane % 32;
+                    const int n = cn0 + cbk * 128 + 4 * c;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = rm0 + ca * 128 + 4 * r + v;
+                        f32x4 o = {acc[ca * 4 + v][cbk * 4 + 0][i], acc[ca * 4 + v][cbk * 4 + 1][i],
+                                   acc[ca * 4 + v][cbk * 4 + 2][i], acc[ca * 4 + v][cbk * 4 + 3][i]};
+                        if (m < p.M) {
+                            float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
+                            if (n + 3 < p.N) {
+                                *(f32x4*)dst = o;
+                            } else {
+#pragma unroll
+                                for (int w = 0; w < 4; ++w)
+                                    if (n + w < p.N) dst[w] = o[w];
+                            }
+                        }
+                    }
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+                    const int m = rm0 + UA::row(i, r);
+                    const int n = cn0 + UB::row(j, lane % 32);
+                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][q]);
+                }
+    }
+}
+
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES>
+struct F32DmaInst {
+    template <bool AK, bool BKM>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        Params copy = p;
+        void* args[] = {&copy};
+        return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
+                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+    }
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        switch (layout) {
+        case 0: return go<true, true>(p, s);
+        case 1: return go<true, false>(p, s);
+        case 2: return go<false, true>(p, s);
+        default: return go<false, false>(p, s);
+        }
+    }
+};
+
+}  // namespace mg
