@@ -85,11 +85,25 @@ struct F32Operand {
         return *(const i32x4*)(t + row * RB + swz_chunk<CPR, true>(row, c) * 16);
     }
 
-    // m-contiguous: rows cbase + 4q .. 4q+3 (q = lane%32) at k = kb + 4h + e.
+    // m-contiguous: rows cbase + RV*q .. RV*q + RV-1 (q = lane%32) at k = kb + 4h + e,
+    // read with one 32-, 64- or 128-bit LDS load (RV = 1, 2, 4).
+    template <int RV>
     __device__ __forceinline__ i32x4 frag_m(const char* t, int cbase, int kb, int e, int lane) const
     {
         const int k = kb + 4 * (lane / 32) + e;
-        return *(const i32x4*)(t + k * RBM + (cbase + 4 * (lane % 32)) * ES);
+        const char* q = t + k * RBM + (cbase + RV * (lane % 32)) * ES;
+        i32x4 r = {0, 0, 0, 0};
+        if constexpr (RV == 4) {
+            r = *(const i32x4*)q;
+        } else if constexpr (RV == 2) {
+            typedef int i32x2 __attribute__((ext_vector_type(2)));
+            const i32x2 v = *(const i32x2*)q;
+            r[0] = v[0];
+            r[1] = v[1];
+        } else {
+            r[0] = *(const int*)q;
+        }
+        return r;
     }
 
     template <int NT>
@@ -109,14 +123,21 @@ struct F32Operand {
     }
 };
 
-// Units of an operand within a wave tile: k-contiguous -> WT/32 row blocks of
-// 32 rows; m-contiguous -> WT/128 blocks of 128 rows x 4 row variants.
+// Units of an operand within a wave tile (WT rows): k-contiguous -> WT/32 row
+// blocks of 32 rows; m-contiguous -> blocks of 32*RV rows, each read as RV
+// interleaved row variants (RV = 4 when WT is a multiple of 128, else 2 or 1).
 template <bool KMAJ, int WT>
 struct Units {
-    static_assert(KMAJ ? WT % 32 == 0 : WT % 128 == 0, "wave tile size for this layout");
+    static_assert(WT % 32 == 0, "wave tile must be a multiple of 32");
     static constexpr int N = WT / 32;
-    // global row (relative to the wave tile) of MFMA row index r in unit u
-    __device__ static __forceinline__ int row(int u, int r) { return KMAJ ? u * 32 + r : (u / 4) * 128 + 4 * r + (u % 4); }
+    static constexpr int RV = KMAJ ? 1 : (WT % 128 == 0 ? 4 : WT % 64 == 0 ? 2 : 1);
+    static constexpr int BLK = 32 * RV;       // rows per block
+    static constexpr int NBLK = WT / BLK;
+    // row (relative to the wave tile) of MFMA row index r in unit u
+    __device__ static __forceinline__ int row(int u, int r)
+    {
+        return KMAJ ? u * 32 + r : (u / RV) * BLK + RV * r + (u % RV);
+    }
 };
 
 template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
@@ -203,10 +224,10 @@ gemm_f32dma_kernel(Params p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int cb = 0; cb < NA / 4; ++cb) {
-                        const i32x4 f = oa.frag_m(sa, wm * WTM + cb * 128, kb, e, lane);
+                    for (int cb = 0; cb < UA::NBLK; ++cb) {
+                        const i32x4 f = oa.template frag_m<UA::RV>(sa, wm * WTM + cb * UA::BLK, kb, e, lane);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) va[buf][e][cb * 4 + v] = f[v];
+                        for (int v = 0; v < UA::RV; ++v) va[buf][e][cb * UA::RV + v] = f[v];
                     }
             }
             if constexpr (BKM) {
@@ -220,14 +241,14 @@ gemm_f32dma_kernel(Params p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int cb = 0; cb < NB / 4; ++cb) {
-                        const i32x4 f = ob.frag_m(sb, wn * WTN + cb * 128, kb, e, lane);
+                    for (int cb = 0; cb < UB::NBLK; ++cb) {
+                        const i32x4 f = ob.template frag_m<UB::RV>(sb, wn * WTN + cb * UB::BLK, kb, e, lane);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) vb[buf][e][cb * 4 + v] = f[v];
+                        for (int v = 0; v < UB::RV; ++v) vb[buf][e][cb * UB::RV + v] = f[v];
                     }
             }
         };
-        constexpr int RA = AK ? NA : NA, RB_ = BKM ? NB : NB;   // 128-bit reads per step
+        constexpr int RA = AK ? NA : 4 * UA::NBLK, RB_ = BKM ? NB : 4 * UB::NBLK;   // LDS reads per step
         read(0, 0);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -254,7 +275,7 @@ gemm_f32dma_kernel(Params p)
 
     // Epilogue.  D row r of unit u maps to tile row UA::row(u, r); likewise columns.
     const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
-    if constexpr (!AK && !BKM && TO == Out::F32) {
+    if constexpr (!AK && !BKM && TO == Out::F32 && UA::RV == 4 && UB::RV == 4) {
         // Both interleaved: for register index i a lane holds rows 4r .. 4r+3 of
         // each 128-row block and columns 4c .. 4c+3 -> 128-bit row stores.
 #pragma unroll

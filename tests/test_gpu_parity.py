@@ -211,3 +211,32 @@ def test_large_integer_sums_stay_exact():
     # K * 25 < 2^24: every fp32 partial sum is an exact integer.
     prob = gi.problem(64, 96, 20000, "k", "n", "n", "f32", "int5", seed=12)
     full_check(prob, exact=True)
+
+
+def test_graph_capture_and_replay():
+    """gemm_run enqueued under HIP graph capture: every replay (with eager work
+    and synchronisation between replays) reproduces the eager result."""
+    import torch
+
+    import dense_gemm_engineering_run_amd as g
+    prob = gi.problem(300, 260, 200, "m", "k", "n", "f16_f32", "int5", seed=21)
+    ref_c, _, st = gu.run(prob)
+    assert st == 0
+    a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+    c = gu.c_buffer(prob)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    args = (prob["M"], prob["N"], prob["K"], "m", "k", "n", prob["dtype"], a.data_ptr(),
+            b.data_ptr(), c.data_ptr(), prob["lda"], prob["ldb"], prob["ldc"], s.cuda_stream)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            assert g.gemm_run(*args) == 0
+    torch.cuda.synchronize()
+    for rep in range(4):
+        c.fill_(0)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got, _ = gu.host_c(c, prob)
+        assert np.array_equal(got.view(np.uint32), ref_c.view(np.uint32)), rep
