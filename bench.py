@@ -51,6 +51,14 @@ for _a in "km":
                 4096, 4096, 4096, _a, _b, _c, "f16_f32", "n01", None,
                 f"fp16 GEMM 4096^3 -> fp32, A {_a}, B {_b}, C {_c}, normal(0,1)")
 
+# The fp16 -> fp16 sweep M = N = 8192, K = 512 .. 16384 with B stored K x N
+# row-major (= N x K n-major here), the persistent-matmul benchmark of the
+# Triton Gluon multi-CTA tutorial.
+for _k in (512, 1024, 2048, 4096, 8192, 16384):
+    WORKLOADS[f"fp16_sweep_k{_k}"] = (
+        8192, 8192, _k, "k", "n", "n", "f16_f16", "n01", None,
+        f"fp16 GEMM 8192x8192x{_k} -> fp16, A k, B n, C n, normal(0,1)")
+
 HEADLINE = "fp32_8192"
 
 
@@ -249,7 +257,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--others", default="all",
-                    help="comma list of extra workloads to time, 'all' or 'none'")
+                    help="comma list of extra workloads to time, 'all' (the five workloads' "
+                         "others), 'sweep' (the fp16 K sweep) or 'none'")
     ap.add_argument("--other-steps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables it)")
@@ -315,9 +324,15 @@ def main():
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         record["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
 
-    others = [] if args.others == "none" else (
-        [w for w in WORKLOADS if w != args.workload] if args.others == "all"
-        else [w for w in args.others.split(",") if w])
+    default_others = [w for w in WORKLOADS if w != args.workload and not w.startswith("fp16_sweep")]
+    if args.others == "none":
+        others = []
+    elif args.others == "all":
+        others = default_others
+    elif args.others == "sweep":
+        others = [w for w in WORKLOADS if w.startswith("fp16_sweep")]
+    else:
+        others = [w for w in args.others.split(",") if w]
     if others:
         record["workloads"] = {}
         del head

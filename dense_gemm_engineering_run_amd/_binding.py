@@ -50,6 +50,8 @@ _i64, _int, _chr, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_char, ctypes.c_vo
 _RUN_ARGS = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.gemm_run.argtypes = _RUN_ARGS
 _lib.gemm_run.restype = _int
+_lib.gemm_run_batched.argtypes = _RUN_ARGS[:-1] + [_i64, _i64, _i64, _i64, _vp]
+_lib.gemm_run_batched.restype = _int
 _lib.gemm_run_config.argtypes = _RUN_ARGS + [_int]
 _lib.gemm_run_config.restype = _int
 _lib.gemm_status_str.argtypes = [_int]
@@ -91,6 +93,13 @@ def gemm_run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, 
     """C ABI gemm_run; A, B, C and stream are integer addresses. Returns the status."""
     return _lib.gemm_run(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
                          lda, ldb, ldc, stream)
+
+
+def gemm_run_batched(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, batch,
+                     stride_a, stride_b, stride_c, stream=0):
+    """C ABI gemm_run_batched (strides in elements). Returns the status."""
+    return _lib.gemm_run_batched(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                                 lda, ldb, ldc, batch, stride_a, stride_b, stride_c, stream)
 
 
 def gemm_run_config(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,

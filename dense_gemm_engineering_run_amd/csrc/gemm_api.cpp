@@ -63,6 +63,7 @@ struct Canon {
     const void* B;
     int64_t lda, ldb, ldc;
     uint64_t a_bytes, b_bytes;
+    int64_t batch, sa, sb, sc;   // batch count and strides in elements
 };
 
 // Bytes spanned by `outer` rows of `ld` elements whose last row holds
@@ -89,11 +90,12 @@ bool overlap(const void* p, uint64_t pn, const void* q, uint64_t qn)
 
 int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char& c_major,
              int dtype, const void* A, const void* B, const void* C, int64_t lda, int64_t ldb,
-             int64_t ldc)
+             int64_t ldc, int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0)
 {
     const int64_t kMaxDim = (int64_t)1 << 30;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_BAD_SHAPE;
+    if (batch < 0 || batch > 65535) return GEMM_ERR_BAD_SHAPE;
     a_major = (char)std::tolower((unsigned char)a_major);
     b_major = (char)std::tolower((unsigned char)b_major);
     c_major = (char)std::tolower((unsigned char)c_major);
@@ -109,19 +111,27 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
     if (lda < std::max<int64_t>(1, a_inner) || ldb < std::max<int64_t>(1, b_inner) ||
         ldc < std::max<int64_t>(1, c_inner))
         return GEMM_ERR_BAD_LD;
+    // Batch strides: non-negative; C entries must not overlap one another.
+    const uint64_t cn = written_extent(c_outer, c_inner, ldc, eo);
+    if (sa < 0 || sb < 0 || sc < 0) return GEMM_ERR_BAD_LD;
+    if (batch > 1 && M > 0 && N > 0 && (uint64_t)sc * eo < cn) return GEMM_ERR_BAD_LD;
 
-    const bool reads = M > 0 && N > 0 && K > 0;
-    const bool writes = M > 0 && N > 0;
+    const bool reads = M > 0 && N > 0 && K > 0 && batch > 0;
+    const bool writes = M > 0 && N > 0 && batch > 0;
     if ((reads && (!A || !B)) || (writes && !C)) return GEMM_ERR_NULL_PTR;
 
     if (reads && (((uintptr_t)A | (uintptr_t)B) & 15)) return GEMM_ERR_MISALIGNED;
     if (writes && ((uintptr_t)C & 15)) return GEMM_ERR_MISALIGNED;
     if ((lda * es) % 16 || (ldb * es) % 16 || (ldc * eo) % 16) return GEMM_ERR_MISALIGNED;
+    if ((sa * es) % 16 || (sb * es) % 16 || (sc * eo) % 16) return GEMM_ERR_MISALIGNED;
 
     if (writes) {
-        uint64_t cn = written_extent(c_outer, c_inner, ldc, eo);
-        if (reads && (overlap(C, cn, A, padded_extent(a_outer, a_inner, lda, es)) ||
-                      overlap(C, cn, B, padded_extent(b_outer, b_inner, ldb, es))))
+        // Whole ranges spanned by all batch entries (conservative).
+        const uint64_t ca = padded_extent(a_outer, a_inner, lda, es);
+        const uint64_t cb = padded_extent(b_outer, b_inner, ldb, es);
+        const uint64_t ct = cn + (uint64_t)(batch - 1) * sc * eo;
+        if (reads && (overlap(C, ct, A, ca + (uint64_t)(batch - 1) * sa * es) ||
+                      overlap(C, ct, B, cb + (uint64_t)(batch - 1) * sb * es)))
             return GEMM_ERR_ALIAS;
     }
     return GEMM_OK;
@@ -142,6 +152,8 @@ Canon canonicalise(int64_t M, int64_t N, int64_t K, char a, char b, char c, int 
         x.B = B; x.ldb = ldb; x.b = b;
     }
     x.ldc = ldc;
+    x.batch = 1;
+    x.sa = x.sb = x.sc = 0;
     const int es = kDtypes[dtype].in_bytes;
     x.a_bytes = x.a == 'k' ? padded_extent(x.M, x.K, x.lda, es) : padded_extent(x.K, x.M, x.lda, es);
     x.b_bytes = x.b == 'k' ? padded_extent(x.N, x.K, x.ldb, es) : padded_extent(x.K, x.N, x.ldb, es);
@@ -282,6 +294,10 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream)
     p.lda = x.lda; p.ldb = x.ldb; p.ldc = x.ldc;
     p.a_bytes = x.K > 0 ? x.a_bytes : 0;
     p.b_bytes = x.K > 0 ? x.b_bytes : 0;
+    p.batch = (int)x.batch;
+    p.sA = x.sa * es;
+    p.sB = x.sb * es;
+    p.sC = x.sc * kDtypes[dtype].out_bytes;
     const int layout = (x.a == 'k' ? 0 : 2) + (x.b == 'k' ? 0 : 1);
     hipError_t err = e.launch(layout, p, (hipStream_t)stream);
     if (err != hipSuccess) return GEMM_ERR_HIP;
@@ -290,18 +306,23 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream)
 }
 
 int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
-        const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config)
+        const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config,
+        int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0)
 {
     t_last_config = -1;
-    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc);
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc);
     if (st != GEMM_OK) return st;
     if (config >= 0) {
         int n = 0;
         entries(dtype, &n);
         if (config >= n) return GEMM_ERR_NO_CONFIG;
     }
-    if (M == 0 || N == 0) return GEMM_OK;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc);
+    x.batch = batch;
+    x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
+    x.sb = c == 'm' ? sa : sb;
+    x.sc = sc;
     if (config < 0) config = select(dtype, a, b, c, M, N, K);
     return launch(x, dtype, C, config, stream);
 }
@@ -315,6 +336,15 @@ int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c
              void* stream)
 {
     return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream, -1);
+}
+
+int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                     int dtype, const void* A, const void* B, void* C, int64_t lda, int64_t ldb,
+                     int64_t ldc, int64_t batch, int64_t stride_a, int64_t stride_b,
+                     int64_t stride_c, void* stream)
+{
+    return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream, -1, batch,
+               stride_a, stride_b, stride_c);
 }
 
 int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,

@@ -230,6 +230,7 @@ gemm_dma_kernel(Params p)
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
+    select_batch(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
@@ -343,7 +344,7 @@ struct DmaInst {
         Params copy = p;
         void* args[] = {&copy};
         return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM>,
-                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+                               dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {

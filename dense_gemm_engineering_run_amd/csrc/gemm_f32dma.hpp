@@ -160,6 +160,7 @@ gemm_f32dma_kernel(Params p)
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
+    select_batch(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
@@ -327,7 +328,7 @@ struct F32DmaInst {
         Params copy = p;
         void* args[] = {&copy};
         return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
-                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+                               dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {

@@ -66,10 +66,21 @@ struct Params {
     int M, N, K;
     int tiles_m, tiles_n;
     int group_m;          // tile rows per raster group
+    int batch;            // number of batch entries (grid.y)
     int64_t lda, ldb, ldc;  // elements
-    uint64_t a_bytes;     // readable extent of A / B in bytes
+    uint64_t a_bytes;     // readable extent of A / B in bytes (one batch entry)
     uint64_t b_bytes;
+    int64_t sA, sB, sC;   // batch strides in bytes (grid.y = batch index)
 };
+
+// Point A, B, C at this workgroup's batch entry.
+__device__ __forceinline__ void select_batch(Params& p)
+{
+    const int64_t l = blockIdx.y;
+    p.A += l * p.sA;
+    p.B += l * p.sB;
+    p.C += l * p.sC;
+}
 
 // Third dword of a buffer resource on gfx9-family parts: 32-bit data format,
 // raw (unswizzled) addressing.
@@ -457,6 +468,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(Params p)
 {
     using T = GemmTile<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>;
+    select_batch(p);
     __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
 
     T t;
@@ -557,7 +569,7 @@ struct Inst {
         Params copy = p;
         void* args[] = {&copy};
         return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>,
-                               dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WM * WN * 64), args, 0, s);
+                               dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {

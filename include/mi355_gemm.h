@@ -68,10 +68,10 @@ typedef enum {
 
 typedef enum {
     GEMM_OK = 0,
-    GEMM_ERR_BAD_SHAPE = 1,    /* M, N or K negative, or a size too large for 32-bit tile indexing */
+    GEMM_ERR_BAD_SHAPE = 1,    /* M, N, K or batch negative, or too large for the tile indexing */
     GEMM_ERR_BAD_MAJOR = 2,    /* major character not in {k,m} / {k,n} / {n,m}          */
     GEMM_ERR_BAD_DTYPE = 3,    /* dtype not a gemm_dtype_t                               */
-    GEMM_ERR_BAD_LD = 4,       /* ld smaller than the contiguous extent (or than 1)      */
+    GEMM_ERR_BAD_LD = 4,       /* ld below the contiguous extent (or 1); bad batch stride */
     GEMM_ERR_NULL_PTR = 5,     /* A or B NULL while M*N*K > 0, or C NULL while M*N > 0   */
     GEMM_ERR_MISALIGNED = 6,   /* pointer not 16-byte aligned, or ld*elem not 16-byte multiple */
     GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */
@@ -88,6 +88,23 @@ typedef enum {
 int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
              int dtype, const void* A, const void* B, void* C,
              int64_t lda, int64_t ldb, int64_t ldc, void* stream);
+
+/*
+ * Strided batched form: for l < batch, C_l = A_l * B_l^T with
+ * A_l = A + l*stride_a, B_l = B + l*stride_b, C_l = C + l*stride_c (strides in
+ * elements).  This is the "L" mode of the CuTe DSL Ampere SGEMM example, whose
+ * run() documents an (M, N, K, L) problem size.  Strides must be >= 0 and
+ * their byte sizes multiples of 16; stride_a or stride_b may be 0 (the same
+ * operand for every entry); C entries must not overlap (stride_c covers one
+ * C, else GEMM_ERR_BAD_LD); batch <= 65535 (else GEMM_ERR_BAD_SHAPE); batch
+ * == 0 launches nothing.  Aliasing is checked over the whole range each
+ * operand spans.  gemm_run is the batch == 1 case.
+ */
+int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                     int dtype, const void* A, const void* B, void* C,
+                     int64_t lda, int64_t ldb, int64_t ldc,
+                     int64_t batch, int64_t stride_a, int64_t stride_b, int64_t stride_c,
+                     void* stream);
 
 /*
  * Same as gemm_run but with an explicit tile config (0 <= config_id <

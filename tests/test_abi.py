@@ -80,6 +80,28 @@ def test_degenerate_sizes_without_gpu():
     assert g.gemm_last_config() == -1
 
 
+def run_batched(batch=2, sa=64 * 64, sb=64 * 64, sc=64 * 64, M=64, N=64, K=64, A=P, B=2 * P,
+                C=3 * P):
+    return g.gemm_run_batched(M, N, K, "k", "k", "n", 0, A, B, C, K, K, N, batch, sa, sb, sc, 0)
+
+
+def test_batched_validation_without_gpu():
+    assert run_batched(batch=-1) == b.GEMM_ERR_BAD_SHAPE
+    assert run_batched(batch=65536) == b.GEMM_ERR_BAD_SHAPE
+    assert run_batched(sa=-64) == b.GEMM_ERR_BAD_LD
+    assert run_batched(sc=64 * 64 - 4) == b.GEMM_ERR_BAD_LD     # C entries would overlap
+    assert run_batched(sc=0) == b.GEMM_ERR_BAD_LD               # ... also when identical
+    assert run_batched(sa=2) == b.GEMM_ERR_MISALIGNED           # 8-byte stride
+    assert run_batched(sc=64 * 64 + 2) == b.GEMM_ERR_MISALIGNED
+    # A's entries reach into C's range: entry 2 of A starts at 3P.
+    assert run_batched(batch=3, sa=(1 << 20) // 4) == b.GEMM_ERR_ALIAS
+    # batch 0 launches nothing and needs no pointers; strides may then be anything >= 0.
+    assert run_batched(batch=0, A=NULL, B=NULL, C=NULL, sc=0) == b.GEMM_OK
+    # Broadcast operands (stride 0) and an empty M pass validation without a launch.
+    assert run_batched(M=0, sa=0, sb=0, sc=0) == b.GEMM_OK
+    assert g.gemm_last_config() == -1
+
+
 def test_majors_case_insensitive():
     assert run(a="X") == b.GEMM_ERR_BAD_MAJOR
     assert run(M=0, a="K", bm="N", c="M", ldc=4) == b.GEMM_OK

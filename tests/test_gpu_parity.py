@@ -240,3 +240,122 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         got, _ = gu.host_c(c, prob)
         assert np.array_equal(got.view(np.uint32), ref_c.view(np.uint32)), rep
+
+
+# ---------------------------------------------------------------- second workload: fp16 K sweep
+
+@pytest.mark.parametrize("K,kind,exact", [(512, "n01", False), (16384, "n01", False), (2048, "int5", True)])
+def test_fp16_out_sweep_8192(K, kind, exact):
+    """M = N = 8192, fp16 in and out, A k-major, B n-major (B stored K x N
+    row-major), C n-major; sampled row blocks against the oracle rounded to fp16."""
+    log(f"sweep f16_f16 8192x8192x{K} knn {kind}")
+    prob = gi.problem(8192, 8192, K, "k", "n", "n", "f16_f16", kind)
+    info = sampled_check(prob, exact, blocks=gu.sample_blocks(8192, size=8))
+    log(f"  {info}")
+
+
+# ---------------------------------------------------------------- strided batched ("L") mode
+
+_GAP_BITS16 = np.uint16(0x7FFF)      # NaN in both fp16 and bf16
+
+
+def _pack(arrs, shared):
+    """Concatenate per-entry storage with a NaN gap between entries; stride 0
+    when every entry is the same array.  Returns (flat array, stride)."""
+    n = arrs[0].size
+    per = 16 // arrs[0].itemsize
+    if shared:
+        return arrs[0], 0
+    stride = -(-n // per) * per + 2 * per
+    fill = np.float32(np.nan) if arrs[0].dtype == np.float32 else _GAP_BITS16
+    buf = np.full(stride * (len(arrs) - 1) + n, fill, dtype=arrs[0].dtype)
+    for i, a in enumerate(arrs):
+        buf[i * stride: i * stride + n] = a
+    return buf, stride
+
+
+def batched_case(M, N, K, layout, dtype, kind, batch, share="", rows=None, seed=11):
+    """Run one strided-batched call and compare every entry with the oracle.
+    share: "a" and/or "b" give that operand stride 0 (one matrix for all).
+    rows: row blocks to compare (None: all rows)."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    a_m, b_m, c_m = layout
+    probs = [gi.problem(M, N, K, a_m, b_m, c_m, dtype, kind, seed=seed + l) for l in range(batch)]
+    for key in ("A", "B"):
+        if key.lower() in share:
+            for p in probs:
+                p[key] = probs[0][key]
+    A, sa = _pack([p["A"] for p in probs], "a" in share)
+    B, sb = _pack([p["B"] for p in probs], "b" in share)
+    p0 = probs[0]
+    outer = N if p0["c_first"] else M
+    per_out = 16 // gi.ELEM_BYTES[p0["out_type"]]
+    sc = outer * p0["ldc"] + 2 * per_out
+    c = gu.c_buffer(dict(p0, ldc=1, M=sc * (batch - 1) + outer * p0["ldc"], N=1, c_first=False))
+    s = torch.cuda.current_stream()
+    a_dev, b_dev = gu.to_device(A), gu.to_device(B)
+    st = g.gemm_run_batched(M, N, K, a_m, b_m, c_m, p0["dtype"], a_dev.data_ptr(),
+                            b_dev.data_ptr(), c.data_ptr(), p0["lda"], p0["ldb"], p0["ldc"],
+                            batch, sa, sb, sc, s.cuda_stream)
+    assert st == 0, g.gemm_status_str(st)
+    cfg = g.gemm_last_config()
+    s.synchronize()
+    flat = c.cpu().numpy()
+    if p0["out_type"] != "f32":
+        flat = flat.view(np.uint16)
+    sentinel = gu.SENTINEL[p0["out_type"]]
+    for l, p in enumerate(probs):
+        part = flat[l * sc: l * sc + outer * p["ldc"]]
+        got = gi.load(part, M, N, p["c_first"], p["ldc"])
+        blocks = rows or [(0, M)]
+        ref = np.concatenate([gu.reference(p, rows=b) for b in blocks])
+        sub = np.concatenate([got[b0:b1] for b0, b1 in blocks])
+        ok, info = gu.check(np.ascontiguousarray(sub), ref, p, kind == "int5")
+        assert ok, (l, info)
+        assert gu.padding_intact(part, p), l
+        gap = flat[l * sc + outer * p["ldc"]: (l + 1) * sc] if l + 1 < batch else flat[:0]
+        assert np.all(gap.view(np.uint32 if p["out_type"] == "f32" else np.uint16) == sentinel), l
+    return cfg
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_batched_every_layout(dtype):
+    """Three entries of a ragged 200x136x72 problem, integer inputs: bit-exact
+    per entry, NaN between entries never read, C gaps never written."""
+    for layout in LAYOUTS8:
+        log(f"batched {dtype} {''.join(layout)} 200x136x72 x3")
+        batched_case(200, 136, 72, layout, dtype, "int5", 3)
+
+
+@pytest.mark.parametrize("share", ["a", "b", "ab"])
+def test_batched_broadcast_operand(share):
+    log(f"batched broadcast {share}")
+    batched_case(96, 160, 40, ("k", "n", "n"), "f32", "int5", 4, share=share)
+    batched_case(96, 160, 40, ("m", "k", "m"), "f16_f32", "u11", 3, share=share)
+
+
+@pytest.mark.parametrize("dtype,layout", [("f32", "mnn"), ("f32", "kkn"), ("f16_f32", "kkn"),
+                                          ("f16_f32", "mnm"), ("bf16_bf16", "kkn")])
+def test_batched_direct_to_lds_kernels(dtype, layout):
+    """Shapes large enough for the direct-to-LDS kernels; sampled rows."""
+    import dense_gemm_engineering_run_amd as g
+    log(f"batched large {dtype} {layout}")
+    cfg = batched_case(4096, 4096, 104, tuple(layout), dtype, "int5", 2,
+                       rows=gu.sample_blocks(4096, size=8))
+    name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
+    log(f"  config {name}")
+    assert name.endswith("dma"), name
+
+
+def test_batched_k_zero_and_empty():
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    c = torch.full((3 * 64 * 32,), 7.0, device="cuda")
+    st = g.gemm_run_batched(64, 32, 0, "k", "k", "n", 0, 0, 0, c.data_ptr(), 4, 4, 32, 3, 0, 0,
+                            64 * 32, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(c).item() == 0
+    st = g.gemm_run_batched(64, 32, 8, "k", "k", "n", 0, 0, 0, 0, 8, 8, 32, 0, 0, 0, 0, 0)
+    assert st == 0
