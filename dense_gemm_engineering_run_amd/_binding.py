@@ -52,6 +52,11 @@ _lib.gemm_run.argtypes = _RUN_ARGS
 _lib.gemm_run.restype = _int
 _lib.gemm_run_batched.argtypes = _RUN_ARGS[:-1] + [_i64, _i64, _i64, _i64, _vp]
 _lib.gemm_run_batched.restype = _int
+_lib.gemm_run_ws.argtypes = _RUN_ARGS[:-1] + [_vp, ctypes.c_size_t, _vp, _int]
+_lib.gemm_run_ws.restype = _int
+_lib.gemm_workspace_size.argtypes = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _int,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+_lib.gemm_workspace_size.restype = _int
 _lib.gemm_run_config.argtypes = _RUN_ARGS + [_int]
 _lib.gemm_run_config.restype = _int
 _lib.gemm_status_str.argtypes = [_int]
@@ -76,7 +81,7 @@ DTYPE_NAMES = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"]
 # gemm_status_t
 (GEMM_OK, GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR, GEMM_ERR_BAD_DTYPE, GEMM_ERR_BAD_LD,
  GEMM_ERR_NULL_PTR, GEMM_ERR_MISALIGNED, GEMM_ERR_ALIAS, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP,
- GEMM_ERR_TUNING_FILE) = range(11)
+ GEMM_ERR_TUNING_FILE, GEMM_ERR_WORKSPACE) = range(12)
 
 
 class GemmError(RuntimeError):
@@ -100,6 +105,23 @@ def gemm_run_batched(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ld
     """C ABI gemm_run_batched (strides in elements). Returns the status."""
     return _lib.gemm_run_batched(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
                                  lda, ldb, ldc, batch, stride_a, stride_b, stride_c, stream)
+
+
+def gemm_run_ws(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, workspace,
+                workspace_bytes, stream=0, config_id=-1):
+    """C ABI gemm_run_ws. Returns the status."""
+    return _lib.gemm_run_ws(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                            lda, ldb, ldc, workspace, workspace_bytes, stream, config_id)
+
+
+def gemm_workspace_size(M, N, K, a_major, b_major, c_major, dtype, config_id=-1):
+    """Workspace bytes for gemm_run_ws; raises GemmError on invalid arguments."""
+    n = ctypes.c_size_t(0)
+    st = _lib.gemm_workspace_size(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype,
+                                  config_id, ctypes.byref(n))
+    if st != GEMM_OK:
+        raise GemmError(st)
+    return n.value
 
 
 def gemm_run_config(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,

@@ -90,7 +90,8 @@ bool overlap(const void* p, uint64_t pn, const void* q, uint64_t qn)
 
 int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char& c_major,
              int dtype, const void* A, const void* B, const void* C, int64_t lda, int64_t ldb,
-             int64_t ldc, int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0)
+             int64_t ldc, int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0,
+             const void* ws = nullptr, size_t ws_bytes = 0)
 {
     const int64_t kMaxDim = (int64_t)1 << 30;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
@@ -124,14 +125,18 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
     if (writes && ((uintptr_t)C & 15)) return GEMM_ERR_MISALIGNED;
     if ((lda * es) % 16 || (ldb * es) % 16 || (ldc * eo) % 16) return GEMM_ERR_MISALIGNED;
     if ((sa * es) % 16 || (sb * es) % 16 || (sc * eo) % 16) return GEMM_ERR_MISALIGNED;
+    if (ws && ((uintptr_t)ws & 15)) return GEMM_ERR_MISALIGNED;
 
     if (writes) {
         // Whole ranges spanned by all batch entries (conservative).
         const uint64_t ca = padded_extent(a_outer, a_inner, lda, es);
         const uint64_t cb = padded_extent(b_outer, b_inner, ldb, es);
         const uint64_t ct = cn + (uint64_t)(batch - 1) * sc * eo;
-        if (reads && (overlap(C, ct, A, ca + (uint64_t)(batch - 1) * sa * es) ||
-                      overlap(C, ct, B, cb + (uint64_t)(batch - 1) * sb * es)))
+        const uint64_t at = ca + (uint64_t)(batch - 1) * sa * es;
+        const uint64_t bt = cb + (uint64_t)(batch - 1) * sb * es;
+        if (reads && (overlap(C, ct, A, at) || overlap(C, ct, B, bt))) return GEMM_ERR_ALIAS;
+        if (ws && ws_bytes &&
+            (overlap(ws, ws_bytes, C, ct) || (reads && (overlap(ws, ws_bytes, A, at) || overlap(ws, ws_bytes, B, bt)))))
             return GEMM_ERR_ALIAS;
     }
     return GEMM_OK;
@@ -269,7 +274,78 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
 
 thread_local int t_last_config = -1;
 
-int launch(const Canon& x, int dtype, void* C, int config, void* stream)
+// Stream-K schedule of a persistent config (mg::KernelEntry::sk_occ > 0).
+// The grid is a fixed 256 CUs x sk_occ workgroups: nothing in the kernel
+// waits for another workgroup, so correctness never depends on how many of
+// them are resident at once.
+constexpr int kSkCUs = 256;
+
+struct SkPlan {
+    int grid = 0, sk_first = 0, sk_tiles = 0, sk_wgs = 0, sk_base = 0, sk_rem = 0;
+    uint64_t count_bytes = 0, bytes = 0;   // counters; whole workspace
+    bool ok = true;                        // false: schedule does not fit 32-bit indexing
+};
+
+SkPlan sk_plan(const mg::KernelEntry& e, int64_t tiles, int64_t nkt)
+{
+    SkPlan s;
+    s.grid = kSkCUs * e.sk_occ;
+    s.sk_first = (int)tiles;
+    if (nkt == 0 || tiles % s.grid == 0) return s;          // whole waves: data-parallel only
+    // The tiles of the last, partial wave share their k-iterations.  Every
+    // stream-K workgroup gets at least ceil(nkt / 8) of them, so a tile has at
+    // most nine contributors (the last one adds up the others' partial
+    // tiles).  Their count is a multiple of 8 (one share per XCD).
+    const int64_t skt = tiles % s.grid;
+    const int64_t iters = skt * nkt;
+    if (iters >= ((int64_t)1 << 31) - nkt) { s.ok = false; return s; }
+    const int64_t min_iters = (nkt + 7) / 8;
+    int64_t wgs = std::min<int64_t>(s.grid, std::max<int64_t>(1, iters / min_iters));
+    if (wgs >= 8) wgs -= wgs % 8;
+    s.sk_first = (int)(tiles - skt);
+    s.sk_tiles = (int)skt;
+    s.sk_wgs = (int)wgs;
+    s.sk_base = (int)(iters / wgs);
+    s.sk_rem = (int)(iters % wgs);
+    s.count_bytes = ((uint64_t)skt * 4 + 255) / 256 * 256;
+    s.bytes = s.count_bytes + 2ull * wgs * e.BM * e.BN * 4;
+    return s;
+}
+
+// Workspace a config needs for the canonical problem x (0 when none).
+uint64_t workspace_need(const mg::KernelEntry& e, int64_t M, int64_t N, int64_t K)
+{
+    if (e.sk_occ == 0) return 0;
+    const int64_t tiles = ((M + e.BM - 1) / e.BM) * ((N + e.BN - 1) / e.BN);
+    return sk_plan(e, tiles, (K + e.BK - 1) / e.BK).bytes;
+}
+
+bool is_sk(int dtype, int config)
+{
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    return config >= 0 && config < n && all[config].sk_occ > 0;
+}
+
+// The config gemm_run* launches when none is forced: the table's choice,
+// unless it is a stream-K config that cannot run here (batched call, or no
+// workspace of the size it needs), then the built-in heuristic.
+int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
+               uint64_t ws_bytes)
+{
+    int config = select(dtype, a, b, c, M, N, K);
+    if (is_sk(dtype, config)) {
+        int n = 0;
+        const mg::KernelEntry& e = entries(dtype, &n)[config];
+        const bool swap = c == 'm';
+        if (batch != 1 || workspace_need(e, swap ? N : M, swap ? M : N, K) > ws_bytes)
+            config = swap ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
+    }
+    return config;
+}
+
+int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* ws = nullptr,
+           uint64_t ws_bytes = 0)
 {
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
@@ -298,6 +374,25 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream)
     p.sA = x.sa * es;
     p.sB = x.sb * es;
     p.sC = x.sc * kDtypes[dtype].out_bytes;
+    p.grid = 0;
+    p.sk_first = p.sk_wgs = p.sk_base = p.sk_rem = 0;
+    p.sk_part = nullptr;
+    p.sk_count = nullptr;
+    if (e.sk_occ > 0) {
+        if (x.batch != 1) return GEMM_ERR_NO_CONFIG;
+        const SkPlan sp = sk_plan(e, tiles_m * tiles_n, (x.K + e.BK - 1) / e.BK);
+        if (!sp.ok) return GEMM_ERR_BAD_SHAPE;
+        if (sp.bytes > 0 && (!ws || ws_bytes < sp.bytes)) return GEMM_ERR_WORKSPACE;
+        p.grid = sp.grid;
+        p.sk_first = sp.sk_first;
+        p.sk_wgs = sp.sk_wgs;
+        p.sk_base = sp.sk_base;
+        p.sk_rem = sp.sk_rem;
+        if (sp.bytes > 0) {
+            p.sk_count = (int*)ws;
+            p.sk_part = (float*)((char*)ws + sp.count_bytes);
+        }
+    }
     const int layout = (x.a == 'k' ? 0 : 2) + (x.b == 'k' ? 0 : 1);
     hipError_t err = e.launch(layout, p, (hipStream_t)stream);
     if (err != hipSuccess) return GEMM_ERR_HIP;
@@ -307,10 +402,12 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream)
 
 int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
         const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config,
-        int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0)
+        int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0, void* ws = nullptr,
+        size_t ws_bytes = 0)
 {
     t_last_config = -1;
-    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc);
+    if (!ws) ws_bytes = 0;
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes);
     if (st != GEMM_OK) return st;
     if (config >= 0) {
         int n = 0;
@@ -323,8 +420,8 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
     x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
     x.sb = c == 'm' ? sa : sb;
     x.sc = sc;
-    if (config < 0) config = select(dtype, a, b, c, M, N, K);
-    return launch(x, dtype, C, config, stream);
+    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes);
+    return launch(x, dtype, C, config, stream, ws, ws_bytes);
 }
 
 }  // namespace
@@ -347,6 +444,35 @@ int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major
                stride_a, stride_b, stride_c);
 }
 
+int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major, int dtype,
+                const void* A, const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc,
+                void* workspace, size_t workspace_bytes, void* stream, int config_id)
+{
+    return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,
+               config_id < 0 ? -1 : config_id, 1, 0, 0, 0, workspace, workspace_bytes);
+}
+
+int gemm_workspace_size(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                        int dtype, int config_id, size_t* bytes)
+{
+    if (!bytes) return GEMM_ERR_NULL_PTR;
+    *bytes = 0;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
+    char a = (char)std::tolower((unsigned char)a_major);
+    char b = (char)std::tolower((unsigned char)b_major);
+    char c = (char)std::tolower((unsigned char)c_major);
+    if ((a != 'k' && a != 'm') || (b != 'k' && b != 'n') || (c != 'n' && c != 'm'))
+        return GEMM_ERR_BAD_MAJOR;
+    if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return GEMM_ERR_BAD_DTYPE;
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    if (config_id >= n) return GEMM_ERR_NO_CONFIG;
+    if (config_id < 0) config_id = select(dtype, a, b, c, M, N, K);
+    const bool swap = c == 'm';
+    *bytes = (size_t)workspace_need(all[config_id], swap ? N : M, swap ? M : N, K);
+    return GEMM_OK;
+}
+
 int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                     int dtype, const void* A, const void* B, void* C, int64_t lda, int64_t ldb,
                     int64_t ldc, void* stream, int config_id)
@@ -362,7 +488,7 @@ const char* gemm_status_str(int status)
 {
     switch (status) {
     case GEMM_OK: return "ok";
-    case GEMM_ERR_BAD_SHAPE: return "bad shape: M, N or K negative or too large";
+    case GEMM_ERR_BAD_SHAPE: return "bad shape: M, N, K or batch negative or too large";
     case GEMM_ERR_BAD_MAJOR: return "bad major: a in {k,m}, b in {k,n}, c in {n,m}";
     case GEMM_ERR_BAD_DTYPE: return "bad dtype";
     case GEMM_ERR_BAD_LD: return "bad leading dimension: smaller than the contiguous extent";
@@ -372,6 +498,7 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_NO_CONFIG: return "no such tile config for this dtype";
     case GEMM_ERR_HIP: return "HIP runtime error at launch";
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
+    case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
     default: return "unknown status";
     }
 }
@@ -404,7 +531,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, char a_major, char b_maj
     if ((a != 'k' && a != 'm') || (b != 'k' && b != 'n') || (c != 'n' && c != 'm'))
         return -GEMM_ERR_BAD_MAJOR;
     if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return -GEMM_ERR_BAD_DTYPE;
-    return select(dtype, a, b, c, M, N, K);
+    return select_for(dtype, a, b, c, M, N, K, 1, 0);
 }
 
 int gemm_last_config(void) { return t_last_config; }

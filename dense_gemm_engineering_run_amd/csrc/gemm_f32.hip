@@ -13,7 +13,12 @@ namespace mg {
     {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma",               \
      BM, BN, BK, WM, WN, 32, true, &F32DmaInst<Out::F32, BM, BN, BK, WM, WN, ST>::launch, ST, true},
 
-static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIGS(MG_F32DMA_ENTRY)};
+#define MG_F32DMA_SK_ENTRY(BM, BN, BK, WM, WN, ST, OCC)                               \
+    {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma sk",            \
+     BM, BN, BK, WM, WN, 32, true, &F32DmaInst<Out::F32, BM, BN, BK, WM, WN, ST, true>::launch, ST, true, OCC},
+
+static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIGS(MG_F32DMA_ENTRY)
+                                           MG_F32DMA_SK_CONFIGS(MG_F32DMA_SK_ENTRY)};
 
 const KernelEntry* entries_f32(int* n)
 {

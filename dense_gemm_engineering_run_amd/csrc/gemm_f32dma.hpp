@@ -140,193 +140,411 @@ struct Units {
     }
 };
 
+// The pieces of the kernel: a main loop over a range of k-tiles of one C tile,
+// and the epilogue that stores a C tile.
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
+struct F32Dma {
+    static constexpr int NW = WM * WN, NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    using UA = Units<AK, WTM>;
+    using UB = Units<BKM, WTN>;
+    static constexpr int NA = UA::N, NB = UB::N;
+    static constexpr int NG = BK / 8;                  // 8-k steps per tile
+    using OA = F32Operand<BM, BK, NW, AK>;
+    using OB = F32Operand<BN, BK, NW, BKM>;
+    static constexpr int STAGE = OA::BYTES + OB::BYTES;
+    static constexpr int LPT = OA::IPW + OB::IPW;
+    static constexpr int SMEM = STAGES * STAGE;
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(STAGES >= 2 && SMEM <= 160 * 1024, "LDS budget");
+    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
+    typedef f32x16 Acc[NA][NB];
+
+    __device__ static __forceinline__ void zero(Acc& acc)
+    {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+    }
+
+    // Accumulate k-tiles [kt0, kt1) of the C tile at (m0, n0) into acc.  The
+    // LDS ring must be free on entry (no wave still reading it); on return
+    // every load has landed.
+    __device__ static __forceinline__ void mainloop(const Params& p, char* smem, OA& oa, OB& ob,
+                                                    int m0, int n0, int kt0, int kt1, Acc& acc, int tid,
+                                                    int lane, int wave)
+    {
+        const int wm = wave / WN, wn = wave % WN;
+        const int nkt = (p.K + BK - 1) / BK;
+        const int kvalid_last = p.K - (nkt - 1) * BK;
+        // Operand fields as locals: read through `p` they would be reloaded
+        // after every DMA asm statement (memory clobber) and the buffer
+        // descriptors rebuilt per k-group.
+        const char* const A = p.A;
+        const char* const B = p.B;
+        const uint64_t a_bytes = p.a_bytes, b_bytes = p.b_bytes;
+        const int64_t lda = p.lda, ldb = p.ldb;
+        const bool ragged = kvalid_last != BK;
+
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) {
+            if (kt0 + s < kt1) {
+                char* st = smem + s * STAGE;
+                oa.issue(A, a_bytes, lda, m0, (kt0 + s) * BK, st, wave);
+                ob.issue(B, b_bytes, ldb, n0, (kt0 + s) * BK, st + OA::BYTES, wave);
+            }
+        }
+
+        for (int t = kt0; t < kt1; ++t) {
+            const int r = t - kt0;
+            const int later = min(STAGES - 2, kt1 - 1 - t);
+            if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
+            else wait_vmcnt_rt(LPT * later);
+            char* st = smem + (r % STAGES) * STAGE;
+            if (t == nkt - 1 && ragged && (AK || BKM)) {
+                bare_barrier();
+                oa.template zero_tail<NT>(st, kvalid_last, tid);
+                ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+            }
+            bare_barrier();
+            const bool more = t + STAGES - 1 < kt1;
+            char* nst = smem + ((r + STAGES - 1) % STAGES) * STAGE;
+            const int nk0 = (t + STAGES - 1) * BK;
+            const char* sa = st;
+            const char* sb = st + OA::BYTES;
+
+            // Fragments of one 8-k step: va[buf][e][u] is the A value of unit u for
+            // k sub-index e; the next step's fragments are read during this step.
+            int va[2][4][NA], vb[2][4][NB];
+            auto read = [&](int g, int buf) {
+                const int kb = g * 8;
+                if constexpr (AK) {
+#pragma unroll
+                    for (int u = 0; u < NA; ++u) {
+                        const i32x4 f = oa.frag_k(sa, wm * WTM + u * 32, kb, lane);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) va[buf][e][u] = f[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int cb = 0; cb < UA::NBLK; ++cb) {
+                            const i32x4 f = oa.template frag_m<UA::RV>(sa, wm * WTM + cb * UA::BLK, kb, e, lane);
+#pragma unroll
+                            for (int v = 0; v < UA::RV; ++v) va[buf][e][cb * UA::RV + v] = f[v];
+                        }
+                }
+                if constexpr (BKM) {
+#pragma unroll
+                    for (int u = 0; u < NB; ++u) {
+                        const i32x4 f = ob.frag_k(sb, wn * WTN + u * 32, kb, lane);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) vb[buf][e][u] = f[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int cb = 0; cb < UB::NBLK; ++cb) {
+                            const i32x4 f = ob.template frag_m<UB::RV>(sb, wn * WTN + cb * UB::BLK, kb, e, lane);
+#pragma unroll
+                            for (int v = 0; v < UB::RV; ++v) vb[buf][e][cb * UB::RV + v] = f[v];
+                        }
+                }
+            };
+            constexpr int RA = AK ? NA : 4 * UA::NBLK, RB_ = BKM ? NB : 4 * UB::NBLK;   // LDS reads per step
+            read(0, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) {
+                    oa.issue(A, a_bytes, lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
+                    ob.issue(B, b_bytes, ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
+                             (g + 1) * OB::IPW / NG);
+                }
+                if (g + 1 < NG) read(g + 1, (g + 1) & 1);
+                const int b = g & 1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < NA; ++i)
+#pragma unroll
+                        for (int j = 0; j < NB; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(va[b][e][i]),
+                                                                              __int_as_float(vb[b][e][j]), acc[i][j], 0, 0, 0);
+                if (g + 1 < NG) interleave<4 * NA * NB, RA + RB_, 0, 0>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Store the C tile at (m0, n0).  D row r of unit u maps to tile row
+    // UA::row(u, r); likewise columns.
+    // COHERENT: write with device-scope cache policy (partial tiles of the
+    // stream-K kernel, read by a workgroup that may sit on another XCD).
+    template <bool COHERENT = false>
+    __device__ static __forceinline__ void store(const Params& p, int m0, int n0, const Acc& acc, int lane,
+                                                 int wave)
+    {
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, 0x7fffffff, kBufferFlags);
+        const int wm = wave / WN, wn = wave % WN;
+        const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
+        if constexpr (!AK && !BKM && TO == Out::F32 && UA::RV == 4 && UB::RV == 4) {
+            // Both interleaved: for register index i a lane holds rows 4r .. 4r+3 of
+            // each 128-row block and columns 4c .. 4c+3 -> 128-bit row stores.
+#pragma unroll
+            for (int ca = 0; ca < NA / 4; ++ca)
+#pragma unroll
+                for (int cbk = 0; cbk < NB / 4; ++cbk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int r = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+                        const int c = lane % 32;
+                        const int n = cn0 + cbk * 128 + 4 * c;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int m = rm0 + ca * 128 + 4 * r + v;
+                            f32x4 o = {acc[ca * 4 + v][cbk * 4 + 0][i], acc[ca * 4 + v][cbk * 4 + 1][i],
+                                       acc[ca * 4 + v][cbk * 4 + 2][i], acc[ca * 4 + v][cbk * 4 + 3][i]};
+                            if (COHERENT) {
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), cr,
+                                                                       (m * BN + n) * 4, 0, kDeviceCoherent);
+                            } else if (m < p.M) {
+                                float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
+                                if (n + 3 < p.N) {
+                                    *(f32x4*)dst = o;
+                                } else {
+#pragma unroll
+                                    for (int w = 0; w < 4; ++w)
+                                        if (n + w < p.N) dst[w] = o[w];
+                                }
+                            }
+                        }
+                    }
+        } else if constexpr (COHERENT) {
+            // Whole tile, row pitch BN: Units::row is linear in its row
+            // argument, so each element's offset is a per-lane part plus a
+            // compile-time constant.
+            static_assert(BN % 4 == 0, "row pitch");
+            const int voff = ((rm0 + UA::row(0, (lane / 32) * 4)) * BN + cn0 + UB::row(0, lane % 32)) * 4;
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int soff = (UA::row(i, (q / 4) * 8 + q % 4) * BN + UB::row(j, 0)) * 4;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[i][j][q]), cr, voff, soff,
+                                                              kDeviceCoherent);
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int r = (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+                        const int m = rm0 + UA::row(i, r);
+                        const int n = cn0 + UB::row(j, lane % 32);
+                        if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][q]);
+                    }
+        }
+    }
+
+    static constexpr int PART_BYTES = BM * BN * 4;   // one partial tile, fp32 row-major
+};
+
 template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_f32dma_kernel(Params p)
 {
-    constexpr int NW = WM * WN, NT = NW * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    using UA = Units<AK, WTM>;
-    using UB = Units<BKM, WTN>;
-    constexpr int NA = UA::N, NB = UB::N;
-    constexpr int NG = BK / 8;                  // 8-k steps per tile
-    using OA = F32Operand<BM, BK, NW, AK>;
-    using OB = F32Operand<BN, BK, NW, BKM>;
-    constexpr int STAGE = OA::BYTES + OB::BYTES;
-    constexpr int LPT = OA::IPW + OB::IPW;
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
-
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+    using KT = F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>;
+    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
 
     select_batch(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    OA oa;
-    OB ob;
+    typename KT::OA oa;
+    typename KT::OB ob;
     oa.init(wave, lane, p.lda);
     ob.init(wave, lane, p.ldb);
 
-    f32x16 acc[NA][NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+    typename KT::Acc acc;
+    KT::zero(acc);
+    KT::mainloop(p, smem, oa, ob, m0, n0, 0, (p.K + BK - 1) / BK, acc, tid, lane, wave);
+    KT::store(p, m0, n0, acc, lane, wave);
+}
 
+// Persistent stream-K form of the same kernel, for grids that would leave
+// part of the chip idle in their last wave (the persistent, load-balanced
+// tile scheduling of the Gluon multi-CTA tutorial, "Persistent kernels" and
+// its cluster launch control scheduler, reshaped for CDNA's plain grid).
+//
+// p.grid workgroups run (a multiple of 8; workgroup w runs on XCD w mod 8).
+//  * Tiles [0, sk_first) are data-parallel: logical id g (XCD-major rank of
+//    w) takes tiles g, g + grid, ...
+//  * The k-iterations of the remaining tiles, tile after tile, are split into
+//    sk_wgs contiguous ranges (sk_base or sk_base + 1 iterations each), one
+//    per stream-K id; consecutive ids share an XCD and every XCD gets
+//    sk_wgs / 8 of them.  A workgroup whose range covers a whole tile stores
+//    it directly.  A tile split over several workgroups is finished by the
+//    last one to arrive: every contributor writes its partial tile (fp32,
+//    row-major) to its workspace slot, waits until the writes are
+//    acknowledged, then increments the tile's counter atomically; the one
+//    that sees the count reach the contributor count adds the partial tiles
+//    in contributor order, stores C and resets the counter to zero.  Nobody
+//    waits for anybody, and the order of the sum depends only on the
+//    schedule, so results are deterministic.
+//
+// Coherence: the XCDs' L2 caches are not coherent with each other.  Partial
+// tiles are written and read with device-scope cache policy (sc1, the
+// encoding the compiler gives agent-scope atomic loads and stores), and the
+// counter is an agent-scope atomic issued only after every partial write of
+// the workgroup has completed (s_waitcnt vmcnt(0), then the barrier), so no
+// whole-L2 write-back or invalidate is needed.
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_f32dma_sk_kernel(Params p)
+{
+    using KT = F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>;
+    static_assert(TO == Out::F32, "stream-K partial tiles are fp32");
+    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
+    __shared__ int arrived;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = p.grid;
+    const int xcd = blockIdx.x % 8, rank = blockIdx.x / 8;
+    const int g = xcd * (G / 8) + rank;
     const int nkt = (p.K + BK - 1) / BK;
-    const int kvalid_last = p.K - (nkt - 1) * BK;
-    const bool ragged = kvalid_last != BK;
 
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-        if (s < nkt) {
-            char* st = smem + s * STAGE;
-            oa.issue(p.A, p.a_bytes, p.lda, m0, s * BK, st, wave);
-            ob.issue(p.B, p.b_bytes, p.ldb, n0, s * BK, st + OA::BYTES, wave);
+    typename KT::OA oa;
+    typename KT::OB ob;
+    oa.init(wave, lane, p.lda);
+    ob.init(wave, lane, p.ldb);
+    typename KT::Acc acc;
+
+    // Stream-K id: sk_wgs is a multiple of 8 (or below 8: XCDs 0 .. sk_wgs-1).
+    const int per_xcd = p.sk_wgs >= 8 ? p.sk_wgs / 8 : 1;
+    const bool streams = rank < per_xcd && xcd * per_xcd + rank < p.sk_wgs;
+    const int k = xcd * per_xcd + rank;
+
+    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(p.sk_part, (short)0, 0x7fffffff, kBufferFlags);
+    const int base = p.sk_base, rem = p.sk_rem;
+    auto start = [&](int w) { return w * base + min(w, rem); };
+    auto owner = [&](int i) {
+        const int cut = rem * (base + 1);
+        return i < cut ? i / (base + 1) : rem + (i - cut) / base;
+    };
+    // Work units: this workgroup's data-parallel tiles, then its stream-K range.
+    int L = g;
+    int it = streams ? start(k) : 0;
+    const int end = streams ? start(k + 1) : 0;
+    while (true) {
+        int tile, kt0, kt1, s = -1;
+        if (L < p.sk_first) {
+            tile = L;
+            kt0 = 0;
+            kt1 = nkt;
+            L += G;
+        } else if (it < end) {
+            s = it / nkt;
+            kt0 = it - s * nkt;
+            kt1 = min(nkt, kt0 + (end - it));
+            tile = p.sk_first + s;
+            it += kt1 - kt0;
+        } else {
+            break;
         }
-    }
-
-    for (int t = 0; t < nkt; ++t) {
-        const int later = min(STAGES - 2, nkt - 1 - t);
-        if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
-        else wait_vmcnt_rt(LPT * later);
-        char* st = smem + (t % STAGES) * STAGE;
-        if (t == nkt - 1 && ragged && (AK || BKM)) {
-            bare_barrier();
-            oa.template zero_tail<NT>(st, kvalid_last, tid);
-            ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-        }
-        bare_barrier();
-        const bool more = t + STAGES - 1 < nkt;
-        char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
-        const int nk0 = (t + STAGES - 1) * BK;
-        const char* sa = st;
-        const char* sb = st + OA::BYTES;
-
-        // Fragments of one 8-k step: va[buf][e][u] is the A value of unit u for
-        // k sub-index e; the next step's fragments are read during this step.
-        int va[2][4][NA], vb[2][4][NB];
-        auto read = [&](int g, int buf) {
-            const int kb = g * 8;
-            if constexpr (AK) {
+        int tm, tn;
+        raster(p, tile, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        KT::zero(acc);
+        KT::mainloop(p, smem, oa, ob, m0, n0, kt0, kt1, acc, tid, lane, wave);
+        if (kt0 == 0 && kt1 == nkt) {
+            KT::store(p, m0, n0, acc, lane, wave);
+        } else {
+            const int ts = s * nkt;
+            const int gf = owner(ts), gl = owner(ts + nkt - 1);
+            // Slot of contributor w for this tile: 2w when the tile is w's first
+            // range piece, 2w + 1 when it is its last (w started in an earlier tile).
+            auto slot = [&](int w) { return (2 * w + (start(w) >= ts ? 0 : 1)) * KT::PART_BYTES; };
+            {
+                Params q = p;                 // the partial tile, row-major BM x BN
+                q.C = (char*)p.sk_part + slot(k);
+                q.ldc = BN;
+                KT::template store<true>(q, 0, 0, acc, lane, wave);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+                arrived = __hip_atomic_fetch_add(p.sk_count + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (arrived == gl - gf) {
+                // Last to arrive: C = partial(gf) + ... + partial(gl).  Thread
+                // tid owns the 16-byte chunks tid + NT*u of the row-major
+                // tile; U chunks per batch keep U loads in flight (fewer for
+                // small tiles, whose kernels run two workgroups per CU and
+                // must stay within 256 registers).
+                constexpr int CH = BM * BN / 4 / KT::NT, UMAX = BM * BN > 128 * 128 ? 16 : 8;
+                constexpr int U = CH < UMAX ? CH : UMAX;
+                static_assert(CH % U == 0, "reduction batches");
+#pragma unroll 1
+                for (int b = 0; b < CH; b += U) {
+                    auto load = [&](int w, f32x4 (&v)[U]) {
 #pragma unroll
-                for (int u = 0; u < NA; ++u) {
-                    const i32x4 f = oa.frag_k(sa, wm * WTM + u * 32, kb, lane);
+                        for (int u = 0; u < U; ++u)
+                            v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                 wsr, slot(w) + tid * 16, (b + u) * KT::NT * 16,
+                                                                 kDeviceCoherent));
+                    };
+                    f32x4 sum[U];
+                    load(gf, sum);
+                    for (int w = gf + 1; w <= gl; ++w) {
+                        f32x4 t[U];
+                        load(w, t);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) va[buf][e][u] = f[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int cb = 0; cb < UA::NBLK; ++cb) {
-                        const i32x4 f = oa.template frag_m<UA::RV>(sa, wm * WTM + cb * UA::BLK, kb, e, lane);
-#pragma unroll
-                        for (int v = 0; v < UA::RV; ++v) va[buf][e][cb * UA::RV + v] = f[v];
+                        for (int u = 0; u < U; ++u) sum[u] += t[u];
                     }
-            }
-            if constexpr (BKM) {
 #pragma unroll
-                for (int u = 0; u < NB; ++u) {
-                    const i32x4 f = ob.frag_k(sb, wn * WTN + u * 32, kb, lane);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) vb[buf][e][u] = f[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int cb = 0; cb < UB::NBLK; ++cb) {
-                        const i32x4 f = ob.template frag_m<UB::RV>(sb, wn * WTN + cb * UB::BLK, kb, e, lane);
-#pragma unroll
-                        for (int v = 0; v < UB::RV; ++v) vb[buf][e][cb * UB::RV + v] = f[v];
-                    }
-            }
-        };
-        constexpr int RA = AK ? NA : 4 * UA::NBLK, RB_ = BKM ? NB : 4 * UB::NBLK;   // LDS reads per step
-        read(0, 0);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (more) {
-                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
-                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
-                         (g + 1) * OB::IPW / NG);
-            }
-            if (g + 1 < NG) read(g + 1, (g + 1) & 1);
-            const int b = g & 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int i = 0; i < NA; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(va[b][e][i]),
-                                                                          __int_as_float(vb[b][e][j]), acc[i][j], 0, 0, 0);
-            if (g + 1 < NG) interleave<4 * NA * NB, RA + RB_, 0, 0>();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Epilogue.  D row r of unit u maps to tile row UA::row(u, r); likewise columns.
-    const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
-    if constexpr (!AK && !BKM && TO == Out::F32 && UA::RV == 4 && UB::RV == 4) {
-        // Both interleaved: for register index i a lane holds rows 4r .. 4r+3 of
-        // each 128-row block and columns 4c .. 4c+3 -> 128-bit row stores.
-#pragma unroll
-        for (int ca = 0; ca < NA / 4; ++ca)
-#pragma unroll
-            for (int cbk = 0; cbk < NB / 4; ++cbk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-                    const int c = lane % 32;
-                    const int n = cn0 + cbk * 128 + 4 * c;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = rm0 + ca * 128 + 4 * r + v;
-                        f32x4 o = {acc[ca * 4 + v][cbk * 4 + 0][i], acc[ca * 4 + v][cbk * 4 + 1][i],
-                                   acc[ca * 4 + v][cbk * 4 + 2][i], acc[ca * 4 + v][cbk * 4 + 3][i]};
+                    for (int u = 0; u < U; ++u) {
+                        const int idx = tid + (b + u) * KT::NT;
+                        const int m = m0 + idx / (BN / 4), n = n0 + (idx % (BN / 4)) * 4;
                         if (m < p.M) {
                             float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
                             if (n + 3 < p.N) {
-                                *(f32x4*)dst = o;
+                                *(f32x4*)dst = sum[u];
                             } else {
 #pragma unroll
-                                for (int w = 0; w < 4; ++w)
-                                    if (n + w < p.N) dst[w] = o[w];
+                                for (int e = 0; e < 4; ++e)
+                                    if (n + e < p.N) dst[e] = sum[u][e];
                             }
                         }
                     }
                 }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int r = (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
-                    const int m = rm0 + UA::row(i, r);
-                    const int n = cn0 + UB::row(j, lane % 32);
-                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][q]);
-                }
+                if (tid == 0) __hip_atomic_store(p.sk_count + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        bare_barrier();                       // the LDS ring (and `arrived`) are reused next
     }
 }
 
-template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SK = false>
 struct F32DmaInst {
     template <bool AK, bool BKM>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         Params copy = p;
         void* args[] = {&copy};
+        if constexpr (SK)
+            return hipLaunchKernel((const void*)&gemm_f32dma_sk_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
+                                   dim3((unsigned)p.grid), dim3(WM * WN * 64), args, 0, s);
         return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }

@@ -71,6 +71,13 @@ struct Params {
     uint64_t a_bytes;     // readable extent of A / B in bytes (one batch entry)
     uint64_t b_bytes;
     int64_t sA, sB, sC;   // batch strides in bytes (grid.y = batch index)
+    // Stream-K schedule (persistent kernels only; see gemm_f32dma.hpp).
+    int grid;             // persistent workgroups (0: one workgroup per tile)
+    int sk_first;         // tiles [0, sk_first) are data-parallel, the rest stream-K
+    int sk_wgs;           // workgroups sharing the stream-K k-iterations
+    int sk_base, sk_rem;  // k-iterations per workgroup: sk_base, +1 for the first sk_rem
+    float* sk_part;       // 2 partial tiles per stream-K workgroup
+    int* sk_count;        // one arrival counter per stream-K tile, zero between calls
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -85,6 +92,8 @@ __device__ __forceinline__ void select_batch(Params& p)
 // Third dword of a buffer resource on gfx9-family parts: 32-bit data format,
 // raw (unswizzled) addressing.
 constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of buffer loads and stores: sc1, device (agent) scope.
+constexpr int kDeviceCoherent = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, uint64_t bytes)
 {
@@ -304,20 +313,27 @@ __device__ __forceinline__ void store_out(char* C, int64_t idx, float v)
     }
 }
 
-// Linear workgroup id -> (tile_m, tile_n).
-__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn)
+// Linear tile index L -> (tile row, tile column) in groups of group_m tile rows.
+__device__ __forceinline__ void raster(const Params& p, int L, int& tm, int& tn)
 {
-    const int G = p.tiles_m * p.tiles_n;
-    const int w = blockIdx.x;
-    const int per = G / 8, rem = G % 8;
-    const int x = w % 8, idx = w / 8;
-    const int L = x * per + (x < rem ? x : rem) + idx;   // XCD x owns a contiguous range
     const int width = p.group_m * p.tiles_n;
     const int first = (L / width) * p.group_m;
     const int gsz = min(p.tiles_m - first, p.group_m);
     const int r = L % width;
     tm = first + r % gsz;
     tn = r / gsz;
+}
+
+// Linear workgroup id -> (tile_m, tile_n): the 8 XCDs (workgroup w runs on
+// XCD w mod 8) each own a contiguous range of the raster order.
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn)
+{
+    const int G = p.tiles_m * p.tiles_n;
+    const int w = blockIdx.x;
+    const int per = G / 8, rem = G % 8;
+    const int x = w % 8, idx = w / 8;
+    const int L = x * per + (x < rem ? x : rem) + idx;
+    raster(p, L, tm, tn);
 }
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
@@ -556,7 +572,8 @@ struct KernelEntry {
     bool swz;
     LaunchFn launch;
     int stages;        // LDS ring depth
-    bool dma;          // direct HBM -> LDS loads (16-bit inputs)
+    bool dma;          // direct HBM -> LDS loads
+    int sk_occ;        // stream-K: persistent workgroups per CU (0: one workgroup per tile)
 };
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>

@@ -9,7 +9,7 @@ update_on_change, tune(), benchmark()); the candidates are this library's
 compiled tile configs rather than JIT parameters.
 
 Each candidate is
-  1. launched through gemm_run_config and must report that the config it ran
+  1. launched through gemm_run_config (gemm_run_ws with a workspace for stream-K configs) and must report that the config it ran
      is the one requested (gemm_last_config) -- the notebook's tune() example
      compiles a fixed copy width whatever candidate it is given, which is the
      mistake this check rules out;
@@ -198,7 +198,15 @@ class GpuMeasure:
         C.zero_()
         args = self._args(key, C) + (cid,)
         s = torch.cuda.current_stream()
-        st = g.gemm_run_config(*args)
+        # Stream-K configs run through gemm_run_ws with a zero-filled workspace.
+        need = g.gemm_workspace_size(M, N, K, a, b, c, dt, cid)
+        ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda") if need else None
+
+        def launch(args):
+            if ws is None:
+                return g.gemm_run_config(*args)
+            return g.gemm_run_ws(*args[:-2], ws.data_ptr(), need, args[-2], args[-1])
+        st = launch(args)
         if st != 0:
             return dict(launched=None, error=g.gemm_status_str(st))
         launched = g.gemm_last_config()
@@ -211,19 +219,19 @@ class GpuMeasure:
             args = (M, N, K, a, b, c, dt, self._tdev[0].data_ptr(), self._tdev[1].data_ptr(),
                     C.data_ptr(), self._dev[3], self._dev[4], self._dev[5], s.cuda_stream, cid)
         for _ in range(self.warmup):
-            g.gemm_run_config(*args)
+            launch(args)
         # keep the GPU busy for at least 50 ms before timing (clock ramp-up)
         s.synchronize()
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.05:
             for _ in range(8):
-                g.gemm_run_config(*args)
+                launch(args)
             s.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(self.iters)]
         for e0, e1 in ev:
             e0.record(s)
-            g.gemm_run_config(*args)
+            launch(args)
             e1.record(s)
         s.synchronize()
         t = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]

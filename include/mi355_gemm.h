@@ -77,7 +77,8 @@ typedef enum {
     GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */
     GEMM_ERR_NO_CONFIG = 8,    /* config id out of range for this dtype                  */
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
-    GEMM_ERR_TUNING_FILE = 10  /* tuning table missing or malformed                      */
+    GEMM_ERR_TUNING_FILE = 10, /* tuning table missing or malformed                      */
+    GEMM_ERR_WORKSPACE = 11    /* stream-K config without a large enough workspace       */
 } gemm_status_t;
 
 /*
@@ -107,9 +108,46 @@ int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major
                      void* stream);
 
 /*
+ * gemm_run with a caller-owned device workspace, which lets the stream-K
+ * configs run (persistent workgroups that split the k-iterations of the last
+ * waves of tiles between them, for grids that would leave CUs idle; after the
+ * Gluon multi-CTA tutorial, "Persistent kernels").  config_id < 0 chooses as
+ * gemm_run does, except that a stream-K config named by the tuning table is
+ * used when workspace_bytes covers gemm_workspace_size() for it; config_id >=
+ * 0 forces that config (GEMM_ERR_WORKSPACE if it is a stream-K config and the
+ * workspace is NULL or smaller than it needs).
+ *
+ * The workspace must be 16-byte aligned (else GEMM_ERR_MISALIGNED), must not
+ * overlap A, B or C (GEMM_ERR_ALIAS), and must be zero-filled before its
+ * first use: it holds per-tile arrival counters that every completed call
+ * leaves at zero again, and partial tiles that need no initialisation.  Two
+ * calls that may run at the same time (e.g. on different streams) need
+ * different workspaces.  NULL / 0 is allowed: then this is gemm_run_config
+ * (or gemm_run for config_id < 0).  Results are deterministic for a given
+ * config and shape.  No batched form: stream-K configs take batch == 1.
+ */
+int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                int dtype, const void* A, const void* B, void* C,
+                int64_t lda, int64_t ldb, int64_t ldc,
+                void* workspace, size_t workspace_bytes, void* stream, int config_id);
+
+/*
+ * Bytes of workspace that gemm_run_ws needs for this problem with config
+ * config_id (< 0: the config the tuning table or the heuristic names for it),
+ * written to *bytes; 0 when the config needs none (not stream-K, or its grid
+ * is whole waves).  Host only: no HIP call.  Returns GEMM_OK,
+ * GEMM_ERR_NULL_PTR (bytes NULL), GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR,
+ * GEMM_ERR_BAD_DTYPE or GEMM_ERR_NO_CONFIG.
+ */
+int gemm_workspace_size(int64_t M, int64_t N, int64_t K, char a_major, char b_major,
+                        char c_major, int dtype, int config_id, size_t* bytes);
+
+/*
  * Same as gemm_run but with an explicit tile config (0 <= config_id <
  * gemm_num_configs(dtype)).  Used by the offline tuner and by the tests that
- * cover every config; GEMM_ERR_NO_CONFIG when the id is out of range.
+ * cover every config; GEMM_ERR_NO_CONFIG when the id is out of range,
+ * GEMM_ERR_WORKSPACE for a stream-K config that needs a workspace (use
+ * gemm_run_ws).
  */
 int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                     int dtype, const void* A, const void* B, void* C,
@@ -131,7 +169,8 @@ int gemm_config_describe(int dtype, int config_id, char* buf, size_t len);
 
 /*
  * The config id gemm_run would launch for these arguments (after the
- * C-m-major swap and the table lookup), or a negative gemm_status_t negated
+ * C-m-major swap and the table lookup; never a stream-K config, since
+ * gemm_run has no workspace), or a negative gemm_status_t negated
  * when the arguments are invalid.  Host only: no HIP call.
  */
 int gemm_select_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major,

@@ -60,7 +60,16 @@ def run(prob, config=None, stream=None, dev=None):
     args = (prob["M"], prob["N"], prob["K"], prob["a_major"], prob["b_major"], prob["c_major"],
             prob["dtype"], a.data_ptr(), b.data_ptr(), c.data_ptr(), prob["lda"], prob["ldb"],
             prob["ldc"], s.cuda_stream)
-    st = g.gemm_run(*args) if config is None else g.gemm_run_config(*args, config)
+    need = 0 if config is None else g.gemm_workspace_size(
+        prob["M"], prob["N"], prob["K"], prob["a_major"], prob["b_major"], prob["c_major"],
+        prob["dtype"], config)
+    if need:            # a stream-K config: zero-filled workspace of the size it asks for
+        ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda")
+        st = g.gemm_run_ws(*args[:-1], ws.data_ptr(), need, s.cuda_stream, config)
+    elif config is None:
+        st = g.gemm_run(*args)
+    else:
+        st = g.gemm_run_config(*args, config)
     s.synchronize()
     logical, flat = host_c(c, prob)
     return logical, flat, st

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for st in range(11):
+    for st in range(12):
         s = g.gemm_status_str(st)
         assert s and s != "unknown status"
     assert g.gemm_status_str(99) == "unknown status"
@@ -100,6 +100,67 @@ def test_batched_validation_without_gpu():
     # Broadcast operands (stride 0) and an empty M pass validation without a launch.
     assert run_batched(M=0, sa=0, sb=0, sc=0) == b.GEMM_OK
     assert g.gemm_last_config() == -1
+
+
+def sk_config(name):
+    for i in range(g.gemm_num_configs(0)):
+        if g.gemm_config_describe(0, i) == name:
+            return i
+    raise KeyError(name)
+
+
+def test_stream_k_workspace_size_and_errors_without_gpu():
+    sk = sk_config("f32 256x256x32 w2x2 mfma32 s2 dma sk")
+    # 4095 x 2049: 16 x 9 = 144 tiles of 256 x 256 (< 256 workgroups, so all are
+    # stream-K), 33 k-tiles each: 4752 iterations over 256 workgroups; counters
+    # (144 ints -> 768 bytes) plus two 256 KB partial tiles per workgroup.
+    need = g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0, sk)
+    assert need == 768 + 2 * 256 * 256 * 256 * 4
+    # The C-m-major swap exchanges M and N: same tile count.
+    assert g.gemm_workspace_size(2049, 4095, 1028, "k", "k", "m", 0, sk) == need
+    # Whole waves (1024 tiles = 4 x 256) and K = 0 need no workspace.
+    assert g.gemm_workspace_size(8192, 8192, 8192, "m", "n", "n", 0, sk) == 0
+    assert g.gemm_workspace_size(4095, 2049, 0, "k", "k", "n", 0, sk) == 0
+    # 257 tiles: one data-parallel wave, then the last tile's 8 k-iterations
+    # shared by 8 workgroups (at least an eighth of a tile each).
+    n257 = g.gemm_workspace_size(257 * 256, 256, 256, "k", "k", "n", 0, sk)
+    assert n257 == 256 + 2 * 8 * 256 * 256 * 4
+    # Not a stream-K config: no workspace.
+    assert g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0, 0) == 0
+    with pytest.raises(g.GemmError):
+        g.gemm_workspace_size(-1, 2, 3, "k", "k", "n", 0)
+    with pytest.raises(g.GemmError):
+        g.gemm_workspace_size(1, 2, 3, "k", "k", "n", 0, 999)
+
+    def run_ws(ws, nbytes, config=sk, C=3 * P):
+        return g.gemm_run_ws(4095, 2049, 1028, "k", "k", "n", 0, P, P + (1 << 24), C, 1028, 1028,
+                             2052, ws, nbytes, 0, config)
+
+    A_end = P + (1 << 24) + 2049 * 1028 * 4
+    C = 1 << 32
+    assert run_ws(0, 0, C=C) == b.GEMM_ERR_WORKSPACE
+    assert run_ws(1 << 34, need - 16, C=C) == b.GEMM_ERR_WORKSPACE
+    assert run_ws((1 << 34) + 8, need, C=C) == b.GEMM_ERR_MISALIGNED
+    assert run_ws(A_end - 64, need, C=C) == b.GEMM_ERR_ALIAS          # overlaps B
+    assert run_ws(C + 4096, need, C=C) == b.GEMM_ERR_ALIAS            # overlaps C
+    assert g.gemm_run_config(4095, 2049, 1028, "k", "k", "n", 0, P, P + (1 << 24), C, 1028, 1028,
+                             2052, 0, sk) == b.GEMM_ERR_WORKSPACE
+    # Stream-K configs take no batch.
+    assert g.gemm_last_config() == -1
+
+
+def test_select_config_never_returns_stream_k(tmp_path):
+    sk_name = "f32 256x256x32 w2x2 mfma32 s2 dma sk"
+    t = tmp_path / "t.txt"
+    t.write_text(f"f32 k k n 4095 2049 1028 {sk_name}\n")
+    try:
+        assert g.gemm_load_tuning(str(t)) == 0
+        chosen = g.gemm_select_config(4095, 2049, 1028, "k", "k", "n", 0)
+        assert chosen >= 0 and not g.gemm_config_describe(0, chosen).endswith(" sk")
+        # With a workspace the table's stream-K choice is the one sized.
+        assert g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0) > 0
+    finally:
+        g.gemm_load_tuning(os.path.join(ROOT, "dense_gemm_engineering_run_amd", "tuning", "table.txt"))
 
 
 def test_majors_case_insensitive():

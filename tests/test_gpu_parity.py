@@ -359,3 +359,88 @@ def test_batched_k_zero_and_empty():
     assert torch.count_nonzero(c).item() == 0
     st = g.gemm_run_batched(64, 32, 8, "k", "k", "n", 0, 0, 0, 0, 8, 8, 32, 0, 0, 0, 0, 0)
     assert st == 0
+
+
+# ---------------------------------------------------------------- stream-K (persistent) fp32 configs
+
+def _sk_configs():
+    import dense_gemm_engineering_run_amd as g
+    return [i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i).endswith(" sk")]
+
+
+def sk_case(M, N, K, layout, config, kind, ldc=None, rows=None, seed=5):
+    """Run a stream-K config through gemm_run_ws twice (fresh C each time) and
+    compare with the oracle; the second run also checks that the first left
+    the workspace's arrival counters at zero."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    prob = gi.problem(M, N, K, *layout, "f32", kind, seed=seed, ldc=ldc)
+    need = g.gemm_workspace_size(M, N, K, *layout, 0, config)
+    ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda")
+    a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+    outs = []
+    for _ in range(2):
+        c = gu.c_buffer(prob)
+        s = torch.cuda.current_stream()
+        st = g.gemm_run_ws(M, N, K, *layout, 0, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                           prob["lda"], prob["ldb"], prob["ldc"], ws.data_ptr() if need else 0,
+                           need, s.cuda_stream, config)
+        assert st == 0, g.gemm_status_str(st)
+        assert g.gemm_last_config() == config
+        s.synchronize()
+        outs.append(gu.host_c(c, prob))
+    (c0, f0), (c1, f1) = outs
+    assert np.array_equal(f0.view(np.uint32), f1.view(np.uint32)), "not deterministic"
+    assert gu.padding_intact(f0, prob)
+    blocks = rows or [(0, M)]
+    refs = np.concatenate([gu.reference(prob, rows=bk) for bk in blocks])
+    got = np.concatenate([c0[b0:b1] for b0, b1 in blocks])
+    ok, info = gu.check(got, refs, prob, kind == "int5")
+    assert ok, info
+    return need, info
+
+
+def test_stream_k_every_config_every_layout():
+    """Shapes with fewer tiles than persistent workgroups (every tile split
+    over 2-3 workgroups), ragged in M, N and K; full oracle comparison."""
+    import dense_gemm_engineering_run_amd as g
+    for cfg in _sk_configs():
+        for layout in [("k", "k", "n"), ("k", "n", "n"), ("m", "k", "n"), ("m", "n", "n"), ("m", "n", "m")]:
+            log(f"stream-K {g.gemm_config_describe(0, cfg)} {''.join(layout)} 600x520x200")
+            need, _ = sk_case(600, 520, 200, layout, cfg, "int5")
+            assert need > 0
+
+
+@pytest.mark.parametrize("kind,exact", [("int5", True), ("u11", False)])
+def test_stream_k_ragged_workload(kind, exact):
+    """4095x2049x1028, A k, B k, C n with ldc 2052: 144 tiles of 256x256 over
+    256 workgroups; sampled row blocks."""
+    import dense_gemm_engineering_run_amd as g
+    rows = gu.sample_blocks(4095, size=8, seed=1) + gu.sample_blocks(4095, size=8, seed=2)
+    rows = sorted(set(rows))
+    for cfg in _sk_configs():
+        log(f"stream-K ragged {g.gemm_config_describe(0, cfg)} {kind}")
+        sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2052, rows=rows)
+
+
+def test_stream_k_data_parallel_waves_plus_split_tail():
+    """More than two waves of tiles, not whole waves: data-parallel tiles
+    first, then the stream-K share (the tiles of the partial wave).  256x256
+    tiles: 24 x 23 = 552 over 256 workgroups; 128x128 tiles: 34 x 34 = 1156
+    over 512."""
+    import dense_gemm_engineering_run_amd as g
+    for cfg in _sk_configs():
+        name = g.gemm_config_describe(0, cfg)
+        M, N = (6144, 5888) if name.startswith("f32 256") else (4352, 4352)
+        log(f"stream-K dp+sk {name} {M}x{N}x96")
+        sk_case(M, N, 96, ("k", "n", "n"), cfg, "int5", rows=gu.sample_blocks(M, size=8, seed=3))
+
+
+def test_stream_k_whole_waves_and_k_zero_need_no_workspace():
+    import dense_gemm_engineering_run_amd as g
+    cfg = _sk_configs()[0]
+    assert g.gemm_config_describe(0, cfg).startswith("f32 256x256")
+    need, _ = sk_case(4096, 4096, 64, ("k", "k", "n"), cfg, "int5", rows=gu.sample_blocks(4096, 8))
+    assert need == 0
+    need, _ = sk_case(700, 300, 0, ("k", "k", "n"), cfg, "int5")
+    assert need == 0
