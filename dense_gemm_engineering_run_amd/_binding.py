@@ -47,6 +47,12 @@ if len(_hip_runtimes()) > 1:
                       "other HIP library, or load this package first")
 
 _i64, _int, _chr, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_char, ctypes.c_void_p
+class Epilogue(ctypes.Structure):
+    """gemm_epilogue_t: C = act(alpha * A.B^T + beta * C_old + bias)."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("bias", ctypes.c_void_p), ("activation", ctypes.c_int)]
+
+
 _RUN_ARGS = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.gemm_run.argtypes = _RUN_ARGS
 _lib.gemm_run.restype = _int
@@ -54,6 +60,9 @@ _lib.gemm_run_batched.argtypes = _RUN_ARGS[:-1] + [_i64, _i64, _i64, _i64, _vp]
 _lib.gemm_run_batched.restype = _int
 _lib.gemm_run_ws.argtypes = _RUN_ARGS[:-1] + [_vp, ctypes.c_size_t, _vp, _int]
 _lib.gemm_run_ws.restype = _int
+_lib.gemm_run_ex.argtypes = _RUN_ARGS[:-1] + [ctypes.POINTER(Epilogue), _vp, ctypes.c_size_t, _vp,
+                                              _int]
+_lib.gemm_run_ex.restype = _int
 _lib.gemm_workspace_size.argtypes = [_i64, _i64, _i64, _chr, _chr, _chr, _int, _int,
                                      ctypes.POINTER(ctypes.c_size_t)]
 _lib.gemm_workspace_size.restype = _int
@@ -81,7 +90,11 @@ DTYPE_NAMES = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"]
 # gemm_status_t
 (GEMM_OK, GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR, GEMM_ERR_BAD_DTYPE, GEMM_ERR_BAD_LD,
  GEMM_ERR_NULL_PTR, GEMM_ERR_MISALIGNED, GEMM_ERR_ALIAS, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP,
- GEMM_ERR_TUNING_FILE, GEMM_ERR_WORKSPACE) = range(12)
+ GEMM_ERR_TUNING_FILE, GEMM_ERR_BAD_EPILOGUE, GEMM_ERR_WORKSPACE) = range(13)
+
+# gemm_activation_t
+GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU = range(3)
+
 
 
 class GemmError(RuntimeError):
@@ -112,6 +125,14 @@ def gemm_run_ws(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ld
     """C ABI gemm_run_ws. Returns the status."""
     return _lib.gemm_run_ws(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
                             lda, ldb, ldc, workspace, workspace_bytes, stream, config_id)
+
+
+def gemm_run_ex(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, epilogue=None,
+                workspace=0, workspace_bytes=0, stream=0, config_id=-1):
+    """C ABI gemm_run_ex; `epilogue` is an Epilogue or None. Returns the status."""
+    epi = ctypes.byref(epilogue) if epilogue is not None else None
+    return _lib.gemm_run_ex(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                            lda, ldb, ldc, epi, workspace, workspace_bytes, stream, config_id)
 
 
 def gemm_workspace_size(M, N, K, a_major, b_major, c_major, dtype, config_id=-1):

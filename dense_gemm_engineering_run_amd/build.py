@@ -2,10 +2,16 @@
 
 Every source under csrc/ is compiled with hipcc for --offload-arch=gfx950 into
 _build/, in parallel, and linked into ``libmi355_gemm.so`` beside this file.
-Packed-fp32 instructions are disabled for all device code.
+Packed-fp32 instructions are disabled for all device code.  The build fails if
+a kernel spills more than SPILL_LIMIT bytes per lane to scratch memory (the
+compiler's resource-usage remarks are checked): accumulators spilled around a
+GEMM main loop cost several times its runtime.  The limit admits the few
+values (up to 8) that the plain 16-bit-output epilogues of the 256x256 tiles
+park in scratch at the loop exit, which cost nothing measurable.
 """
 import glob
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -18,22 +24,40 @@ LIB = os.path.join(HERE, "libmi355_gemm.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SPILL_LIMIT = 32        # bytes of scratch per lane
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wno-inline-asm",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+def _spills(remarks):
+    """(function, scratch bytes per lane) for every kernel whose ScratchSize in
+    hipcc's kernel-resource-usage remarks exceeds SPILL_LIMIT."""
+    bad, fn = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            fn = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > SPILL_LIMIT:
+            bad.append((fn, int(m.group(1))))
+    return bad
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{out}")
-    if out.strip() and verbose:
-        print(out)
+    bad = _spills(out)
+    if bad:
+        raise RuntimeError(f"register spills in {src}: " + ", ".join(f"{f} ({b} B/lane)" for f, b in bad))
+    if verbose:
+        print("\n".join(l for l in out.splitlines() if "remark" not in l))
     return obj
 
 

@@ -91,7 +91,7 @@ bool overlap(const void* p, uint64_t pn, const void* q, uint64_t qn)
 int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char& c_major,
              int dtype, const void* A, const void* B, const void* C, int64_t lda, int64_t ldb,
              int64_t ldc, int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0,
-             const void* ws = nullptr, size_t ws_bytes = 0)
+             const void* ws = nullptr, size_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr)
 {
     const int64_t kMaxDim = (int64_t)1 << 30;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
@@ -126,6 +126,8 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
     if ((lda * es) % 16 || (ldb * es) % 16 || (ldc * eo) % 16) return GEMM_ERR_MISALIGNED;
     if ((sa * es) % 16 || (sb * es) % 16 || (sc * eo) % 16) return GEMM_ERR_MISALIGNED;
     if (ws && ((uintptr_t)ws & 15)) return GEMM_ERR_MISALIGNED;
+    const float* bias = epi ? epi->bias : nullptr;
+    if (bias && ((uintptr_t)bias & 3)) return GEMM_ERR_MISALIGNED;
 
     if (writes) {
         // Whole ranges spanned by all batch entries (conservative).
@@ -138,6 +140,7 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
         if (ws && ws_bytes &&
             (overlap(ws, ws_bytes, C, ct) || (reads && (overlap(ws, ws_bytes, A, at) || overlap(ws, ws_bytes, B, bt)))))
             return GEMM_ERR_ALIAS;
+        if (bias && overlap(bias, (uint64_t)N * 4, C, ct)) return GEMM_ERR_ALIAS;
     }
     return GEMM_OK;
 }
@@ -327,25 +330,31 @@ bool is_sk(int dtype, int config)
     return config >= 0 && config < n && all[config].sk_occ > 0;
 }
 
+// True when the epilogue does something (else the plain store runs).
+bool epi_active(const gemm_epilogue_t* epi)
+{
+    return epi && (epi->alpha != 1.f || epi->beta != 0.f || epi->bias || epi->activation != GEMM_ACT_NONE);
+}
+
 // The config gemm_run* launches when none is forced: the table's choice,
-// unless it is a stream-K config that cannot run here (batched call, or no
-// workspace of the size it needs), then the built-in heuristic.
+// unless it is a stream-K config that cannot run here (batched call, an
+// epilogue, or no workspace of the size it needs), then the heuristic.
 int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
-               uint64_t ws_bytes)
+               uint64_t ws_bytes, bool epi = false)
 {
     int config = select(dtype, a, b, c, M, N, K);
     if (is_sk(dtype, config)) {
         int n = 0;
         const mg::KernelEntry& e = entries(dtype, &n)[config];
         const bool swap = c == 'm';
-        if (batch != 1 || workspace_need(e, swap ? N : M, swap ? M : N, K) > ws_bytes)
+        if (batch != 1 || epi || workspace_need(e, swap ? N : M, swap ? M : N, K) > ws_bytes)
             config = swap ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
     }
     return config;
 }
 
 int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* ws = nullptr,
-           uint64_t ws_bytes = 0)
+           uint64_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr, bool bias_rows = false)
 {
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
@@ -378,6 +387,12 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     p.sk_first = p.sk_wgs = p.sk_base = p.sk_rem = 0;
     p.sk_part = nullptr;
     p.sk_count = nullptr;
+    p.epi = epi_active(epi);
+    p.alpha = epi ? epi->alpha : 1.f;
+    p.beta = epi ? epi->beta : 0.f;
+    p.bias = epi ? epi->bias : nullptr;
+    p.bias_rows = bias_rows;
+    p.act = epi ? epi->activation : GEMM_ACT_NONE;
     if (e.sk_occ > 0) {
         if (x.batch != 1) return GEMM_ERR_NO_CONFIG;
         const SkPlan sp = sk_plan(e, tiles_m * tiles_n, (x.K + e.BK - 1) / e.BK);
@@ -403,25 +418,28 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
 int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
         const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config,
         int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0, void* ws = nullptr,
-        size_t ws_bytes = 0)
+        size_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr)
 {
     t_last_config = -1;
     if (!ws) ws_bytes = 0;
-    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes);
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes, epi);
     if (st != GEMM_OK) return st;
     if (config >= 0) {
         int n = 0;
         entries(dtype, &n);
         if (config >= n) return GEMM_ERR_NO_CONFIG;
     }
+    if (epi && (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)) return GEMM_ERR_BAD_EPILOGUE;
+    if (epi_active(epi) && is_sk(dtype, config)) return GEMM_ERR_BAD_EPILOGUE;   // stream-K: no epilogue
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc);
     x.batch = batch;
     x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
     x.sb = c == 'm' ? sa : sb;
     x.sc = sc;
-    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes);
-    return launch(x, dtype, C, config, stream, ws, ws_bytes);
+    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, epi_active(epi));
+    // bias follows the user's columns n: the canonical rows when C is m-major.
+    return launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
 }
 
 }  // namespace
@@ -450,6 +468,15 @@ int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, cha
 {
     return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,
                config_id < 0 ? -1 : config_id, 1, 0, 0, 0, workspace, workspace_bytes);
+}
+
+int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major, int dtype,
+                const void* A, const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc,
+                const gemm_epilogue_t* epilogue, void* workspace, size_t workspace_bytes, void* stream,
+                int config_id)
+{
+    return run(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream,
+               config_id < 0 ? -1 : config_id, 1, 0, 0, 0, workspace, workspace_bytes, epilogue);
 }
 
 int gemm_workspace_size(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
@@ -499,6 +526,7 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_HIP: return "HIP runtime error at launch";
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
     case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
+    case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation";
     default: return "unknown status";
     }
 }

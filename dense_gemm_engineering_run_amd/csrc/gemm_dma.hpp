@@ -209,7 +209,9 @@ struct DmaOperand {
     }
 };
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM>
+// EPI: as for gemm_kernel (a separate instantiation for 16-bit outputs that
+// run the elementwise epilogue).
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_dma_kernel(Params p)
 {
@@ -313,6 +315,18 @@ gemm_dma_kernel(Params p)
     }
 
     // Epilogue (as in gemm_kernel): fp32 accumulators -> output type, predicated stores.
+    if (TO == Out::F32 ? p.epi : EPI) {
+        constexpr int R = MI == 32 ? 16 : 4;
+        store_tile_via_lds<TO, BM, BN, NT, TM * TN * R, STAGES * STAGE>(
+            p, smem, m0, n0, tid, [&](int v) { return acc[v / (TN * R)][(v / R) % TN][v % R]; },
+            [&](int v, int& r, int& c) {
+                const int i = v / (TN * R), j = (v / R) % TN, q = v % R;
+                c = wn * WTN + j * MI + (lane % MI);
+                r = wm * WTM + i * MI + (MI == 32 ? (q / 4) * 8 + (lane / 32) * 4 + (q % 4) : (lane / 16) * 4 + q);
+            });
+        return;
+    }
+    if constexpr (TO != Out::F32 && EPI) return;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -338,13 +352,20 @@ gemm_dma_kernel(Params p)
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES>
 struct DmaInst {
-    template <bool AK, bool BKM>
+    template <bool AK, bool BKM, bool EPI>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         Params copy = p;
         void* args[] = {&copy};
-        return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM>,
+        return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM, EPI>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
+    }
+    template <bool AK, bool BKM>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        if constexpr (TO != Out::F32)
+            if (p.epi) return go<AK, BKM, true>(p, s);
+        return go<AK, BKM, false>(p, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {

@@ -285,13 +285,25 @@ struct F32Dma {
     // UA::row(u, r); likewise columns.
     // COHERENT: write with device-scope cache policy (partial tiles of the
     // stream-K kernel, read by a workgroup that may sit on another XCD).
-    template <bool COHERENT = false>
+    // With EPI and p.epi set the tile goes through the elementwise epilogue
+    // via LDS, which must be free (smem = the kernel's LDS ring).
+    template <bool COHERENT = false, bool EPI = true>
     __device__ static __forceinline__ void store(const Params& p, int m0, int n0, const Acc& acc, int lane,
-                                                 int wave)
+                                                 int wave, char* smem = nullptr)
     {
         const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, 0x7fffffff, kBufferFlags);
         const int wm = wave / WN, wn = wave % WN;
         const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
+        if (!COHERENT && EPI && p.epi) {
+            store_tile_via_lds<TO, BM, BN, NT, NA * NB * 16, SMEM>(
+                p, smem, m0, n0, wave * 64 + lane, [&](int v) { return acc[v / (NB * 16)][(v / 16) % NB][v % 16]; },
+                [&](int v, int& r, int& c) {
+                    const int i = v / (NB * 16), j = (v / 16) % NB, q = v % 16;
+                    r = wm * WTM + UA::row(i, (q / 4) * 8 + (lane / 32) * 4 + (q % 4));
+                    c = wn * WTN + UB::row(j, lane % 32);
+                });
+            return;
+        }
         if constexpr (!AK && !BKM && TO == Out::F32 && UA::RV == 4 && UB::RV == 4) {
             // Both interleaved: for register index i a lane holds rows 4r .. 4r+3 of
             // each 128-row block and columns 4c .. 4c+3 -> 128-bit row stores.
@@ -379,7 +391,7 @@ gemm_f32dma_kernel(Params p)
     typename KT::Acc acc;
     KT::zero(acc);
     KT::mainloop(p, smem, oa, ob, m0, n0, 0, (p.K + BK - 1) / BK, acc, tid, lane, wave);
-    KT::store(p, m0, n0, acc, lane, wave);
+    KT::store(p, m0, n0, acc, lane, wave, smem);
 }
 
 // Persistent stream-K form of the same kernel, for grids that would leave
@@ -468,7 +480,7 @@ gemm_f32dma_sk_kernel(Params p)
         KT::zero(acc);
         KT::mainloop(p, smem, oa, ob, m0, n0, kt0, kt1, acc, tid, lane, wave);
         if (kt0 == 0 && kt1 == nkt) {
-            KT::store(p, m0, n0, acc, lane, wave);
+            KT::template store<false, false>(p, m0, n0, acc, lane, wave);
         } else {
             const int ts = s * nkt;
             const int gf = owner(ts), gl = owner(ts + nkt - 1);
@@ -495,20 +507,19 @@ gemm_f32dma_sk_kernel(Params p)
                 constexpr int CH = BM * BN / 4 / KT::NT, UMAX = BM * BN > 128 * 128 ? 16 : 8;
                 constexpr int U = CH < UMAX ? CH : UMAX;
                 static_assert(CH % U == 0, "reduction batches");
+                auto part = [&](int w, int c) {
+                    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         wsr, slot(w) + tid * 16, c * KT::NT * 16, kDeviceCoherent));
+                };
 #pragma unroll 1
                 for (int b = 0; b < CH; b += U) {
-                    auto load = [&](int w, f32x4 (&v)[U]) {
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                 wsr, slot(w) + tid * 16, (b + u) * KT::NT * 16,
-                                                                 kDeviceCoherent));
-                    };
                     f32x4 sum[U];
-                    load(gf, sum);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) sum[u] = part(gf, b + u);
                     for (int w = gf + 1; w <= gl; ++w) {
                         f32x4 t[U];
-                        load(w, t);
+#pragma unroll
+                        for (int u = 0; u < U; ++u) t[u] = part(w, b + u);
 #pragma unroll
                         for (int u = 0; u < U; ++u) sum[u] += t[u];
                     }

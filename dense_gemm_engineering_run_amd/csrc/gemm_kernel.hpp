@@ -78,6 +78,12 @@ struct Params {
     int sk_base, sk_rem;  // k-iterations per workgroup: sk_base, +1 for the first sk_rem
     float* sk_part;       // 2 partial tiles per stream-K workgroup
     int* sk_count;        // one arrival counter per stream-K tile, zero between calls
+    // Elementwise epilogue (store_epi); epi == 0 stores the accumulator as is.
+    int epi;
+    float alpha, beta;    // C = act(alpha * acc + beta * C_old + bias)
+    const float* bias;    // fp32, indexed by column n (by row m when bias_rows), or null
+    int bias_rows;
+    int act;              // Act
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -313,6 +319,131 @@ __device__ __forceinline__ void store_out(char* C, int64_t idx, float v)
     }
 }
 
+template <Out TO>
+__device__ __forceinline__ float load_out(const char* C, int64_t idx)
+{
+    if constexpr (TO == Out::F32) {
+        return ((const float*)C)[idx];
+    } else if constexpr (TO == Out::F16) {
+        return (float)((const _Float16*)C)[idx];
+    } else {
+        return (float)__builtin_bit_cast(__bf16, ((const uint16_t*)C)[idx]);
+    }
+}
+
+// Activations of the epilogue.
+enum Act : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
+
+// erf(x) for the GELU epilogue, inline (a library call in an unrolled
+// epilogue would make the accumulators live across calls and spill them):
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26,
+// |error| <= 1.5e-7:  erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-x^2},
+// t = 1 / (1 + p x) for x >= 0, and erf(-x) = -erf(x).
+__device__ __forceinline__ float erf_as(float x)
+{
+    const float ax = __builtin_fabsf(x);
+    const float t = 1.f / (1.f + 0.3275911f * ax);
+    const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f +
+                                                t * (-1.453152027f + t * 1.061405429f))));
+    const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.44269504088896341f);   // e^{-x^2}
+    const float y = 1.f - poly * e;
+    return x < 0.f ? -y : y;
+}
+
+// Store output element (m, n) of the canonical C through the elementwise
+// epilogue (kernels call this only when p.epi is set, from a loop of its own,
+// so that the plain store path keeps its code).  The SGEMM example applies
+// its epilogue_op to the accumulator fragment right before the store, and CK
+// Tile's kernel has an Epilogue stage after the GEMM.  In fp32:
+//   v = act(alpha * acc + beta * C_old + bias)     (C_old read only if beta != 0)
+// relu(x) = (x < 0 ? 0 : x), which keeps NaN; gelu(x) = x/2 * (1 + erf(x / sqrt 2)),
+// with erf_as above (GELU values within about 1e-7 |x| of the exact ones).
+template <Out TO>
+__device__ __forceinline__ float epi_value(const Params& p, int m, int n, float v)
+{
+    float t = p.alpha * v;
+    if (p.beta != 0.f) t = __builtin_fmaf(p.beta, load_out<TO>(p.C, (int64_t)m * p.ldc + n), t);
+    if (p.bias) t += p.bias[p.bias_rows ? m : n];
+    if (p.act == kActRelu) t = t < 0.f ? 0.f : t;
+    else if (p.act == kActGelu) t = 0.5f * t * (1.f + erf_as(t * 0.70710678118654752f));
+    return t;
+}
+
+template <Out TO>
+__device__ __forceinline__ void store_epi(const Params& p, int m, int n, float v)
+{
+    store_out<TO>(p.C, (int64_t)m * p.ldc + n, epi_value<TO>(p, m, n, v));
+}
+
+// Store 4 consecutive outputs (m, n .. n+3) of the canonical C, given in fp32:
+// through the elementwise epilogue when p.epi is set, then converted; one
+// 128-bit (fp32) or 64-bit (16-bit) store when all four are inside C.
+template <Out TO>
+__device__ __forceinline__ void store4(const Params& p, int m, int n, f32x4 v)
+{
+    if (p.epi) {
+#pragma unroll 1
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) store_epi<TO>(p, m, n + e, v[e]);
+        return;
+    }
+    const int64_t idx = (int64_t)m * p.ldc + n;
+    if (n + 3 < p.N) {
+        if constexpr (TO == Out::F32) {
+            *(f32x4*)((float*)p.C + idx) = v;
+        } else {
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                h[e] = TO == Out::F16 ? __builtin_bit_cast(uint16_t, (_Float16)v[e])
+                                      : __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+            *(u32x2*)((uint16_t*)p.C + idx) = u32x2{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) store_out<TO>(p.C, idx + e, v[e]);
+    }
+}
+
+// Tile epilogue through LDS, for the elementwise epilogue: the tile is
+// handled in bands of RB rows; each lane parks its
+// accumulators of the band at [row][col] in LDS (fp32), then every thread
+// takes runs of 4 values along n and writes them with store4 -- row-major,
+// coalesced vector stores instead of one store per accumulator, and one copy
+// of the epilogue code.  get(v) returns accumulator v (a constant index once
+// the loops are unrolled), pos(v, r, c) its tile-local row and column.  The
+// LDS (LDS_BYTES from smem) must be free: a barrier follows the main loop
+// here before anything is written.
+template <Out TO, int BM, int BN, int NT, int NV, int LDS_BYTES, class Get, class Pos>
+__device__ __forceinline__ void store_tile_via_lds(const Params& p, char* smem, int m0, int n0, int tid,
+                                                   Get get, Pos pos)
+{
+    constexpr int FIT = LDS_BYTES / (BN * 4);
+    constexpr int RB = FIT >= BM ? BM : FIT >= 128 ? 128 : FIT >= 64 ? 64 : FIT >= 32 ? 32 : FIT >= 16 ? 16 : 8;
+    static_assert(FIT >= 8 && BM % RB == 0, "LDS too small for the staged epilogue");
+    float* t = (float*)smem;
+    __syncthreads();
+#pragma unroll
+    for (int b0 = 0; b0 < BM; b0 += RB) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            int r, c;
+            pos(v, r, c);
+            if (r >= b0 && r < b0 + RB) t[(r - b0) * BN + c] = get(v);
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int q = tid; q < RB * BN / 4; q += NT) {
+            const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+            const int m = m0 + b0 + r;
+            if (m < p.M) store4<TO>(p, m, n0 + c, *(const f32x4*)(t + r * BN + c));
+        }
+        __syncthreads();
+    }
+}
+
 // Linear tile index L -> (tile row, tile column) in groups of group_m tile rows.
 __device__ __forceinline__ void raster(const Params& p, int L, int& tm, int& tn)
 {
@@ -479,7 +610,10 @@ struct GemmTile {
     }
 };
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
+// EPI: instantiation that runs the elementwise epilogue (only used for 16-bit
+// outputs, whose plain epilogue and epilogue path do not share a kernel well:
+// together they exhaust the registers; fp32 outputs take both in one kernel).
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(Params p)
 {
@@ -540,6 +674,18 @@ gemm_kernel(Params p)
 
     // Epilogue: fp32 accumulators -> output type, predicated stores.
     constexpr int MI_ = MI;
+    if (TO == Out::F32 ? p.epi : EPI) {
+        constexpr int R = MI_ == 32 ? 16 : 4;
+        store_tile_via_lds<TO, BM, BN, T::NT, T::TM * T::TN * R, 2 * T::STAGE>(
+            p, smem, m0, n0, t.tid, [&](int v) { return t.acc[v / (T::TN * R)][(v / R) % T::TN][v % R]; },
+            [&](int v, int& r, int& c) {
+                const int i = v / (T::TN * R), j = (v / R) % T::TN, q = v % R;
+                c = t.wn * T::WTN + j * MI_ + (lane % MI_);
+                r = t.wm * T::WTM + i * MI_ + (MI_ == 32 ? (q / 4) * 8 + (lane / 32) * 4 + (q % 4) : (lane / 16) * 4 + q);
+            });
+        return;
+    }
+    if constexpr (TO != Out::F32 && EPI) return;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -578,15 +724,22 @@ struct KernelEntry {
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>
 struct Inst {
-    template <bool AK, bool BKM>
+    template <bool AK, bool BKM, bool EPI>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         // hipLaunchKernel reports this launch's own status (a stale error left
         // by an earlier runtime call on the thread cannot be mistaken for it).
         Params copy = p;
         void* args[] = {&copy};
-        return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>,
+        return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ, EPI>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
+    }
+    template <bool AK, bool BKM>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        if constexpr (TO != Out::F32)
+            if (p.epi) return go<AK, BKM, true>(p, s);
+        return go<AK, BKM, false>(p, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {

@@ -78,8 +78,38 @@ typedef enum {
     GEMM_ERR_NO_CONFIG = 8,    /* config id out of range for this dtype                  */
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
     GEMM_ERR_TUNING_FILE = 10, /* tuning table missing or malformed                      */
-    GEMM_ERR_WORKSPACE = 11    /* stream-K config without a large enough workspace       */
+    GEMM_ERR_BAD_EPILOGUE = 11, /* unknown activation, or an epilogue with a stream-K config */
+    GEMM_ERR_WORKSPACE = 12    /* stream-K config without a large enough workspace       */
 } gemm_status_t;
+
+/* Activations of the elementwise epilogue. */
+typedef enum {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,         /* x < 0 ? 0 : x (NaN stays NaN)          */
+    GEMM_ACT_GELU = 2          /* x/2 * (1 + erf(x / sqrt(2)))            */
+} gemm_activation_t;
+
+/*
+ * Elementwise epilogue applied to every output element before the store, in
+ * fp32, as the SGEMM example's epilogue_op is applied to the accumulator
+ * fragment right before it is copied out (identity by default), and as CK
+ * Tile composes a kernel from a problem, a pipeline policy and an Epilogue:
+ *
+ *     C[m][n] = act(alpha * sum_k A[m][k] B[n][k] + beta * C_old[m][n] + bias[n])
+ *
+ * C_old is C's value before the call, in C's type, read only when beta != 0
+ * (beta == 0 ignores whatever C holds, NaN included).  bias is a device
+ * array of N fp32 values (one per column n of C, whatever c_major), 4-byte
+ * aligned, or NULL.  The result is rounded to C's type (RNE) as without an
+ * epilogue.  alpha = 1, beta = 0, bias = NULL, act = GEMM_ACT_NONE is the
+ * plain product.
+ */
+typedef struct {
+    float alpha;
+    float beta;
+    const float* bias;
+    int activation;            /* gemm_activation_t */
+} gemm_epilogue_t;
 
 /*
  * C = A * B^T (storage B is N x K) as described above, with the tile config
@@ -129,6 +159,18 @@ int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major
 int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                 int dtype, const void* A, const void* B, void* C,
                 int64_t lda, int64_t ldb, int64_t ldc,
+                void* workspace, size_t workspace_bytes, void* stream, int config_id);
+
+/*
+ * gemm_run_ws with an elementwise epilogue (NULL: none).  Errors besides
+ * gemm_run_ws's: bias not 4-byte aligned -> GEMM_ERR_MISALIGNED; bias
+ * overlapping C -> GEMM_ERR_ALIAS; unknown activation, or an epilogue that is
+ * not the identity with a forced stream-K config -> GEMM_ERR_BAD_EPILOGUE
+ * (config_id < 0 never picks a stream-K config when the epilogue is active).
+ */
+int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                int dtype, const void* A, const void* B, void* C,
+                int64_t lda, int64_t ldb, int64_t ldc, const gemm_epilogue_t* epilogue,
                 void* workspace, size_t workspace_bytes, void* stream, int config_id);
 
 /*

@@ -11,6 +11,7 @@ docstring; reference check in ``run()``) and the CK Tile practice GEMM README
 ``compare`` implement the acceptance test on top of it.
 """
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -96,4 +97,36 @@ def decode(bits, in_type):
     y = np.empty(bits.shape, dtype=np.float64)
     fn = {"f16": lib.oracle_decode_f16_n, "bf16": lib.oracle_decode_bf16_n}[in_type]
     fn(_ptr(bits), _ptr(y), bits.size)
+    return y
+
+
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+
+
+def epilogue_ref(acc, alpha=1.0, beta=0.0, c_old=None, bias=None, activation=ACT_NONE):
+    """The elementwise epilogue, in fp64, on an M x N array of exact sums:
+
+        act(alpha * acc + beta * c_old + bias[n])
+
+    The SGEMM example applies its ``epilogue_op`` (identity by default) to the
+    accumulator fragment right before copying it out; CK Tile composes a kernel
+    from a problem, a pipeline policy and an Epilogue stage.  The engine's
+    epilogue offers a scale, a scaled read of the old C, a per-column bias and
+    an activation: relu(x) = 0 if x < 0 else x (NaN stays NaN), gelu(x) =
+    x/2 * (1 + erf(x / sqrt 2)) with the library erf.  ``c_old`` (fp64, M x N)
+    is used only when beta != 0.  The caller rounds the result to the output
+    type.
+    """
+    y = alpha * np.asarray(acc, dtype=np.float64)
+    if beta != 0.0:
+        y = y + beta * np.asarray(c_old, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if activation == ACT_RELU:
+        y = np.where(y < 0.0, 0.0, y)
+    elif activation == ACT_GELU:
+        erf = np.vectorize(math.erf, otypes=[np.float64])
+        y = 0.5 * y * (1.0 + erf(y / math.sqrt(2.0)))
+    elif activation != ACT_NONE:
+        raise ValueError(activation)
     return y

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for st in range(12):
+    for st in range(13):
         s = g.gemm_status_str(st)
         assert s and s != "unknown status"
     assert g.gemm_status_str(99) == "unknown status"
@@ -161,6 +161,24 @@ def test_select_config_never_returns_stream_k(tmp_path):
         assert g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0) > 0
     finally:
         g.gemm_load_tuning(os.path.join(ROOT, "dense_gemm_engineering_run_amd", "tuning", "table.txt"))
+
+
+def test_epilogue_errors_without_gpu():
+    def run_ex(epi, C=3 * P):
+        return g.gemm_run_ex(64, 64, 64, "k", "k", "n", 0, P, 2 * P, C, 64, 64, 64, epi)
+    assert run_ex(g.Epilogue(1.0, 0.0, P + 2, 0)) == b.GEMM_ERR_MISALIGNED   # bias not 4-byte aligned
+    assert run_ex(g.Epilogue(1.0, 0.0, 3 * P + 64, 0)) == b.GEMM_ERR_ALIAS   # bias inside C
+    assert run_ex(g.Epilogue(1.0, 0.0, 0, 7)) == b.GEMM_ERR_BAD_EPILOGUE
+    assert run_ex(g.Epilogue(1.0, 0.0, 0, -1)) == b.GEMM_ERR_BAD_EPILOGUE
+    # argument errors come first, in status order
+    assert g.gemm_run_ex(-1, 64, 64, "k", "k", "n", 0, P, 2 * P, 3 * P, 64, 64, 64,
+                         g.Epilogue(1.0, 0.0, 0, 7)) == b.GEMM_ERR_BAD_SHAPE
+    # an empty problem still rejects a bad activation, launches nothing otherwise
+    assert g.gemm_run_ex(0, 64, 64, "k", "k", "n", 0, 0, 0, 0, 64, 64, 64,
+                         g.Epilogue(1.0, 0.0, 0, 7)) == b.GEMM_ERR_BAD_EPILOGUE
+    assert g.gemm_run_ex(0, 64, 64, "k", "k", "n", 0, 0, 0, 0, 64, 64, 64,
+                         g.Epilogue(2.0, 1.0, 0, 1)) == b.GEMM_OK
+    assert g.gemm_last_config() == -1
 
 
 def test_majors_case_insensitive():

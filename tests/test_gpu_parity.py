@@ -444,3 +444,104 @@ def test_stream_k_whole_waves_and_k_zero_need_no_workspace():
     assert need == 0
     need, _ = sk_case(700, 300, 0, ("k", "k", "n"), cfg, "int5")
     assert need == 0
+
+
+# ---------------------------------------------------------------- elementwise epilogue
+
+def _c_storage(c_log_bits, prob):
+    """Flat C storage (outer x ldc) holding logical M x N bits, padding = sentinel."""
+    tout = prob["out_type"]
+    bits = np.uint32 if tout == "f32" else np.uint16
+    outer = prob["N"] if prob["c_first"] else prob["M"]
+    flat = np.full(outer * prob["ldc"], gu.SENTINEL[tout], dtype=bits)
+    view = flat.reshape(outer, prob["ldc"])
+    view[:, :c_log_bits.shape[1] if not prob["c_first"] else c_log_bits.shape[0]] = \
+        (c_log_bits.T if prob["c_first"] else c_log_bits).view(bits)
+    return flat
+
+
+def epi_case(M, N, K, layout, dtype, kind, alpha, beta, act, with_bias=True, config=None, seed=9,
+             nan_c=False, expect=0):
+    """One gemm_run_ex call with an epilogue against oracle.epilogue_ref on the
+    oracle's exact sums.  C starts with integers in [-5, 5] (NaN with nan_c),
+    the bias holds halves in [-4, 4]."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    import oracle
+    prob = gi.problem(M, N, K, *layout, dtype, kind, seed=seed)
+    tout = prob["out_type"]
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    c_old = rng.integers(-5, 6, size=(M, N)).astype(np.float32)
+    if nan_c:
+        c_old[:] = np.nan
+    c_bits = gi.cast(c_old, tout)
+    flat = _c_storage(np.ascontiguousarray(c_bits), prob)
+    c = gu.to_device(flat.view(np.float32) if tout == "f32" else flat)
+    bias = (rng.integers(-8, 9, size=N) / 2).astype(np.float32)
+    bias_dev = torch.from_numpy(bias).cuda()
+    need = g.gemm_workspace_size(M, N, K, *layout, prob["dtype"], -1 if config is None else config)
+    ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda")
+    a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+    s = torch.cuda.current_stream()
+    epi = g.Epilogue(alpha, beta, bias_dev.data_ptr() if with_bias else 0, act)
+    st = g.gemm_run_ex(M, N, K, *layout, prob["dtype"], a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                       prob["lda"], prob["ldb"], prob["ldc"], epi, ws.data_ptr() if need else 0,
+                       need, s.cuda_stream, -1 if config is None else config)
+    if expect:
+        assert st == expect, g.gemm_status_str(st)
+        return None
+    assert st == 0, g.gemm_status_str(st)
+    s.synchronize()
+    got, out_flat = gu.host_c(c, prob)
+    old64 = c_old.astype(np.float64) if tout == "f32" else oracle.decode(c_bits, tout)
+    want = oracle.epilogue_ref(gu.reference(prob), alpha, beta, old64,
+                               bias if with_bias else None, act)
+    ok, info = gu.check(got, want, prob, kind == "int5")
+    assert ok, (layout, dtype, config, info)
+    assert gu.padding_intact(out_flat, prob)
+    return g.gemm_last_config()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_epilogue_every_config_exact(dtype):
+    """alpha = 2, beta = -0.5, per-column bias, relu on integer inputs: every
+    intermediate is exact in fp32, so the result must match bit for bit.
+    C n-major and m-major (the bias then runs along the canonical rows)."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    for cfg in range(g.gemm_num_configs(code)):
+        name = g.gemm_config_describe(code, cfg)
+        expect = g.GEMM_ERR_BAD_EPILOGUE if name.endswith(" sk") else 0   # stream-K: no epilogue
+        for layout in [("k", "k", "n"), ("m", "n", "m")]:
+            epi_case(300, 200, 136, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg,
+                     expect=expect)
+        log(f"{name}: epilogue exact" if not expect else f"{name}: epilogue refused")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
+def test_epilogue_gelu_and_scale(dtype):
+    import dense_gemm_engineering_run_amd as g
+    kind = {"f32": "u11", "f16_f32": "n01", "bf16_bf16": "n002"}[dtype]
+    for layout in LAYOUTS8:
+        epi_case(257, 190, 96, layout, dtype, kind, 0.75, 0.25, g.GEMM_ACT_GELU)
+    log(f"{dtype}: gelu epilogue, 8 layouts")
+
+
+def test_epilogue_beta_zero_ignores_c_and_k_zero():
+    import dense_gemm_engineering_run_amd as g
+    epi_case(200, 120, 64, ("k", "k", "n"), "f32", "int5", 1.0, 0.0, g.GEMM_ACT_NONE, nan_c=True)
+    epi_case(200, 120, 64, ("k", "n", "m"), "bf16_bf16", "int5", -1.0, 0.0, g.GEMM_ACT_RELU,
+             nan_c=True)
+    # K = 0: C = act(beta * C_old + bias)
+    epi_case(130, 70, 0, ("k", "k", "n"), "f32", "int5", 3.0, 2.0, g.GEMM_ACT_NONE)
+
+
+def test_epilogue_large_direct_kernels():
+    """Shapes that take the direct-to-LDS kernels by default (several bands of
+    the staged epilogue per tile, and 16-bit outputs)."""
+    import dense_gemm_engineering_run_amd as g
+    for dtype, layout in [("f32", "mnn"), ("f32", "kkn"), ("f16_f16", "knn"), ("bf16_bf16", "kkm")]:
+        cfg = epi_case(4096, 4096, 64, tuple(layout), dtype, "int5", 2.0, 1.0, g.GEMM_ACT_RELU)
+        name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
+        log(f"  {dtype} {layout}: {name}")
+        assert name.endswith("dma"), name

@@ -336,3 +336,46 @@ def test_inputs_store_load_roundtrip_and_ranges():
         assert np.isnan(buf).sum() == 12 * (100 if first else 300)
     x = np.array([[1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5]], np.float32)
     assert gi.cast(x, "bf16").tolist() == [[0x3F80, 0x3F80, 0x3F82, 0xC020]]
+
+
+# ---------------------------------------------------------------- epilogue
+
+def test_epilogue_hand_worked_example():
+    """alpha, beta and a per-column bias on a 2 x 3 example computed by hand:
+    a swapped alpha/beta, a bias along rows, or a dropped term all fail."""
+    acc = np.array([[1.0, -2.0, 3.0], [4.0, 5.0, -6.0]])
+    c_old = np.array([[10.0, 20.0, 30.0], [40.0, 50.0, 60.0]])
+    bias = np.array([0.5, -1.0, 2.0])
+    y = oracle.epilogue_ref(acc, alpha=2.0, beta=-0.5, c_old=c_old, bias=bias)
+    # row 0: 2 - 5 + 0.5, -4 - 10 - 1, 6 - 15 + 2;  row 1: 8 - 20 + 0.5, 10 - 25 - 1, -12 - 30 + 2
+    assert np.array_equal(y, np.array([[-2.5, -15.0, -7.0], [-11.5, -16.0, -40.0]]))
+    # beta == 0 never reads C (NaN there does not matter); identity by default
+    nan_c = np.full_like(c_old, np.nan)
+    assert np.array_equal(oracle.epilogue_ref(acc, c_old=nan_c), acc)
+    relu = oracle.epilogue_ref(y, activation=oracle.ACT_RELU)
+    assert np.array_equal(relu, np.zeros_like(y))
+    assert np.array_equal(oracle.epilogue_ref(acc, activation=oracle.ACT_RELU),
+                          np.array([[1.0, 0.0, 3.0], [4.0, 5.0, 0.0]]))
+
+
+def test_epilogue_relu_special_values():
+    x = np.array([[np.nan, -0.0, 0.0, -1e-300, np.inf, -np.inf]])
+    y = oracle.epilogue_ref(x, activation=oracle.ACT_RELU)
+    assert np.isnan(y[0, 0])
+    assert np.signbit(y[0, 1]) and y[0, 1] == 0.0          # -0 is not < 0: kept
+    assert y[0, 2] == 0.0 and y[0, 3] == 0.0 and y[0, 4] == np.inf and y[0, 5] == 0.0
+
+
+def test_epilogue_gelu_closed_forms():
+    """gelu(x) = x * Phi(x) with Phi the standard normal CDF: Phi(0) = 1/2,
+    Phi(1) = 0.8413447460685429 and Phi(-x) = 1 - Phi(x) (published values of
+    the normal distribution), Phi(10) = 1 to double precision."""
+    phi1 = 0.8413447460685429
+    x = np.array([[0.0, 1.0, -1.0, 2.0, 10.0, -10.0]])
+    y = oracle.epilogue_ref(x, activation=oracle.ACT_GELU)[0]
+    assert y[0] == 0.0
+    assert abs(y[1] - phi1) < 1e-15
+    assert abs(y[2] + (1.0 - phi1)) < 1e-15
+    assert abs(y[3] - 2.0 * 0.9772498680518208) < 1e-15       # Phi(2)
+    assert y[4] == 10.0
+    assert -1e-21 <= y[5] <= 0.0          # true value -7.6e-23; 1 + erf(-7.07) rounds to 0
