@@ -64,6 +64,7 @@ struct Canon {
     int64_t lda, ldb, ldc;
     uint64_t a_bytes, b_bytes;
     int64_t batch, sa, sb, sc;   // batch count and strides in elements
+    bool vec16;                  // 16-byte loads allowed (else scalar configs only)
 };
 
 // Bytes spanned by `outer` rows of `ld` elements whose last row holds
@@ -88,10 +89,15 @@ bool overlap(const void* p, uint64_t pn, const void* q, uint64_t qn)
     return a < b + qn && b < a + pn;
 }
 
+// Argument checks.  *vec16 reports whether the operands allow 16-byte loads
+// (pointers and leading dimensions and batch strides in 16-byte units); when
+// they do not, only the element-by-element ("scalar") configs can run, and
+// the pointers need only their element alignment.
 int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char& c_major,
              int dtype, const void* A, const void* B, const void* C, int64_t lda, int64_t ldb,
              int64_t ldc, int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0,
-             const void* ws = nullptr, size_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr)
+             const void* ws = nullptr, size_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr,
+             bool* vec16 = nullptr)
 {
     const int64_t kMaxDim = (int64_t)1 << 30;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_BAD_SHAPE;
@@ -121,18 +127,21 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
     const bool writes = M > 0 && N > 0 && batch > 0;
     if ((reads && (!A || !B)) || (writes && !C)) return GEMM_ERR_NULL_PTR;
 
-    if (reads && (((uintptr_t)A | (uintptr_t)B) & 15)) return GEMM_ERR_MISALIGNED;
-    if (writes && ((uintptr_t)C & 15)) return GEMM_ERR_MISALIGNED;
-    if ((lda * es) % 16 || (ldb * es) % 16 || (ldc * eo) % 16) return GEMM_ERR_MISALIGNED;
-    if ((sa * es) % 16 || (sb * es) % 16 || (sc * eo) % 16) return GEMM_ERR_MISALIGNED;
+    if (reads && (((uintptr_t)A | (uintptr_t)B) % es)) return GEMM_ERR_MISALIGNED;
+    if (writes && ((uintptr_t)C % eo)) return GEMM_ERR_MISALIGNED;
     if (ws && ((uintptr_t)ws & 15)) return GEMM_ERR_MISALIGNED;
+    const bool v16 = !(reads && (((uintptr_t)A | (uintptr_t)B) & 15)) && !(writes && ((uintptr_t)C & 15)) &&
+                     (lda * es) % 16 == 0 && (ldb * es) % 16 == 0 && (ldc * eo) % 16 == 0 &&
+                     (sa * es) % 16 == 0 && (sb * es) % 16 == 0 && (sc * eo) % 16 == 0;
+    if (vec16) *vec16 = v16;
     const float* bias = epi ? epi->bias : nullptr;
     if (bias && ((uintptr_t)bias & 3)) return GEMM_ERR_MISALIGNED;
 
     if (writes) {
-        // Whole ranges spanned by all batch entries (conservative).
-        const uint64_t ca = padded_extent(a_outer, a_inner, lda, es);
-        const uint64_t cb = padded_extent(b_outer, b_inner, ldb, es);
+        // Whole ranges spanned by all batch entries (conservative); the
+        // readable extents of the 16-byte path end on a 16-byte chunk.
+        const uint64_t ca = v16 ? padded_extent(a_outer, a_inner, lda, es) : written_extent(a_outer, a_inner, lda, es);
+        const uint64_t cb = v16 ? padded_extent(b_outer, b_inner, ldb, es) : written_extent(b_outer, b_inner, ldb, es);
         const uint64_t ct = cn + (uint64_t)(batch - 1) * sc * eo;
         const uint64_t at = ca + (uint64_t)(batch - 1) * sa * es;
         const uint64_t bt = cb + (uint64_t)(batch - 1) * sb * es;
@@ -147,7 +156,7 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
 
 // C m-major: C^T (N x M, n-major) = B * A^T.  Swap the operands and sizes.
 Canon canonicalise(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype,
-                   const void* A, const void* B, int64_t lda, int64_t ldb, int64_t ldc)
+                   const void* A, const void* B, int64_t lda, int64_t ldb, int64_t ldc, bool vec16 = true)
 {
     Canon x;
     if (c == 'm') {
@@ -163,8 +172,10 @@ Canon canonicalise(int64_t M, int64_t N, int64_t K, char a, char b, char c, int 
     x.batch = 1;
     x.sa = x.sb = x.sc = 0;
     const int es = kDtypes[dtype].in_bytes;
-    x.a_bytes = x.a == 'k' ? padded_extent(x.M, x.K, x.lda, es) : padded_extent(x.K, x.M, x.lda, es);
-    x.b_bytes = x.b == 'k' ? padded_extent(x.N, x.K, x.ldb, es) : padded_extent(x.K, x.N, x.ldb, es);
+    auto ext = vec16 ? padded_extent : written_extent;
+    x.a_bytes = x.a == 'k' ? ext(x.M, x.K, x.lda, es) : ext(x.K, x.M, x.lda, es);
+    x.b_bytes = x.b == 'k' ? ext(x.N, x.K, x.ldb, es) : ext(x.K, x.N, x.ldb, es);
+    x.vec16 = vec16;
     return x;
 }
 
@@ -254,6 +265,23 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K)
     return pick("64x64x64 w2x2 mfma16 s2 swz");
 }
 
+// Built-in choice among the element-by-element configs (operands that are
+// not 16-byte aligned).
+int heuristic_scalar(int dtype, int64_t M, int64_t N)
+{
+    const std::string tile = std::ceil(M / 128.0) * std::ceil(N / 128.0) >= 64
+                                 ? (dtype == GEMM_DTYPE_F32 ? "128x128x16 w2x2 mfma32" : "128x128x64 w2x2 mfma32")
+                                 : (dtype == GEMM_DTYPE_F32 ? "64x64x16 w2x2 mfma16" : "64x64x64 w2x2 mfma16");
+    return find_config(dtype, std::string(kDtypes[dtype].name) + " " + tile + " s2 swz scalar");
+}
+
+bool is_scalar(int dtype, int config)
+{
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    return config >= 0 && config < n && all[config].scalar;
+}
+
 int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
 {
     std::call_once(g_env_once, load_env_table);
@@ -340,8 +368,9 @@ bool epi_active(const gemm_epilogue_t* epi)
 // unless it is a stream-K config that cannot run here (batched call, an
 // epilogue, or no workspace of the size it needs), then the heuristic.
 int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
-               uint64_t ws_bytes, bool epi = false)
+               uint64_t ws_bytes, bool epi = false, bool vec16 = true)
 {
+    if (!vec16) return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
     int config = select(dtype, a, b, c, M, N, K);
     if (is_sk(dtype, config)) {
         int n = 0;
@@ -393,6 +422,7 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     p.bias = epi ? epi->bias : nullptr;
     p.bias_rows = bias_rows;
     p.act = epi ? epi->activation : GEMM_ACT_NONE;
+    p.c_vec = ((uintptr_t)C & 15) == 0 && (x.ldc * kDtypes[dtype].out_bytes) % 16 == 0;
     if (e.sk_occ > 0) {
         if (x.batch != 1) return GEMM_ERR_NO_CONFIG;
         const SkPlan sp = sk_plan(e, tiles_m * tiles_n, (x.K + e.BK - 1) / e.BK);
@@ -422,22 +452,26 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
 {
     t_last_config = -1;
     if (!ws) ws_bytes = 0;
-    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes, epi);
+    bool vec16 = true;
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes, epi,
+                      &vec16);
     if (st != GEMM_OK) return st;
     if (config >= 0) {
         int n = 0;
         entries(dtype, &n);
         if (config >= n) return GEMM_ERR_NO_CONFIG;
+        if (!vec16 && !is_scalar(dtype, config)) return GEMM_ERR_MISALIGNED;   // needs 16-byte loads
     }
     if (epi && (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)) return GEMM_ERR_BAD_EPILOGUE;
     if (epi_active(epi) && is_sk(dtype, config)) return GEMM_ERR_BAD_EPILOGUE;   // stream-K: no epilogue
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
-    Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc);
+    Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc, vec16);
     x.batch = batch;
     x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
     x.sb = c == 'm' ? sa : sb;
     x.sc = sc;
-    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, epi_active(epi));
+    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, epi_active(epi), vec16);
+    if (config < 0) return GEMM_ERR_NO_CONFIG;
     // bias follows the user's columns n: the canonical rows when C is m-major.
     return launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
 }

@@ -84,6 +84,7 @@ struct Params {
     const float* bias;    // fp32, indexed by column n (by row m when bias_rows), or null
     int bias_rows;
     int act;              // Act
+    int c_vec;            // C and ldc allow 16-byte stores (else element stores only)
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -110,6 +111,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, ui
 __device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// The 16 bytes at `off` as one 128-bit load (VEC), or element by element:
+// the SGEMM example falls back to scalar copies when an operand is not
+// 16-byte aligned, and so do the kernels instantiated with VEC = false (each
+// element then only needs its natural alignment; out-of-range elements read 0).
+template <int ES, bool VEC>
+__device__ __forceinline__ i32x4 load_chunk(__amdgpu_buffer_rsrc_t r, int off)
+{
+    if constexpr (VEC) {
+        return buf_load16(r, off);
+    } else if constexpr (ES == 4) {
+        i32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0);
+        return v;
+    } else {
+        i32x4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * d, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * d + 2, 0, 0);
+            v[d] = (int)(lo | (hi << 16));
+        }
+        return v;
+    }
 }
 
 // LDS bank window of gfx950: 64 banks x 4 bytes = 256 bytes = 16 chunks of
@@ -155,7 +182,7 @@ __device__ __forceinline__ i32x4 mask_k(i32x4 v, int k0, int K)
 
 // Operand tile loader: ROWS x BK tile of an operand into LDS rows of BK.
 // KMAJ: the operand's contiguous index is k.
-template <In TI, int ROWS, int BK, int NT, bool KMAJ, bool SWZ>
+template <In TI, int ROWS, int BK, int NT, bool KMAJ, bool SWZ, bool VEC = true>
 struct TileLoader {
     static constexpr int ES = TI == In::F32 ? 4 : 2;   // element bytes
     static constexpr int CE = 16 / ES;                  // elements per chunk
@@ -202,10 +229,10 @@ struct TileLoader {
         for (int i = 0; i < PER; ++i) {
             if (FULL || i * NT + tid < UNITS) {
                 if (KMAJ) {
-                    r[i] = buf_load16(rs, voff[i]);
+                    r[i] = load_chunk<ES, VEC>(rs, voff[i]);
                 } else {
 #pragma unroll
-                    for (int j = 0; j < CE; ++j) r[i * CE + j] = buf_load16(rs, voff[i] + j * ldb);
+                    for (int j = 0; j < CE; ++j) r[i * CE + j] = load_chunk<ES, VEC>(rs, voff[i] + j * ldb);
                 }
             }
         }
@@ -388,7 +415,7 @@ __device__ __forceinline__ void store4(const Params& p, int m, int n, f32x4 v)
         return;
     }
     const int64_t idx = (int64_t)m * p.ldc + n;
-    if (n + 3 < p.N) {
+    if (p.c_vec && n + 3 < p.N) {
         if constexpr (TO == Out::F32) {
             *(f32x4*)((float*)p.C + idx) = v;
         } else {
@@ -488,7 +515,8 @@ __device__ __forceinline__ void interleave()
     }
 }
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ>
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ,
+          bool VEC = true>
 struct GemmTile {
     static constexpr int NT = WM * WN * 64;
     static constexpr int ES = TI == In::F32 ? 4 : 2;
@@ -507,8 +535,8 @@ struct GemmTile {
     static_assert(CPR % NQ == 0, "BK too small for this MFMA shape");
     static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
     using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
-    using LA = TileLoader<TI, BM, BK, NT, AK, SWZ>;
-    using LB = TileLoader<TI, BN, BK, NT, BKM, SWZ>;
+    using LA = TileLoader<TI, BM, BK, NT, AK, SWZ, VEC>;
+    using LB = TileLoader<TI, BN, BK, NT, BKM, SWZ, VEC>;
     static constexpr int NW = (AK ? LA::PER : LA::PER * CE) + (BKM ? LB::PER : LB::PER * CE);
     static constexpr int NL = LA::REGS + LB::REGS;
 
@@ -613,11 +641,12 @@ struct GemmTile {
 // EPI: instantiation that runs the elementwise epilogue (only used for 16-bit
 // outputs, whose plain epilogue and epilogue path do not share a kernel well:
 // together they exhaust the registers; fp32 outputs take both in one kernel).
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ, bool EPI>
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool SWZ, bool EPI,
+          bool VEC>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(Params p)
 {
-    using T = GemmTile<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ>;
+    using T = GemmTile<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ, VEC>;
     select_batch(p);
     __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
 
@@ -720,9 +749,12 @@ struct KernelEntry {
     int stages;        // LDS ring depth
     bool dma;          // direct HBM -> LDS loads
     int sk_occ;        // stream-K: persistent workgroups per CU (0: one workgroup per tile)
+    bool scalar;       // element-by-element loads: any leading dimension, element-aligned pointers
 };
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ>
+// VEC = false: element-by-element operand loads, for operands that are not
+// 16-byte aligned.
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool SWZ, bool VEC = true>
 struct Inst {
     template <bool AK, bool BKM, bool EPI>
     static hipError_t go(const Params& p, hipStream_t s)
@@ -731,7 +763,7 @@ struct Inst {
         // by an earlier runtime call on the thread cannot be mistaken for it).
         Params copy = p;
         void* args[] = {&copy};
-        return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ, EPI>,
+        return hipLaunchKernel((const void*)&gemm_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, SWZ, EPI, VEC>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     template <bool AK, bool BKM>

@@ -24,12 +24,17 @@
  * library keeps no pointer after a call returns and allocates nothing.
  *
  * Alignment (SGEMM example, "Constraints" in its docstring: the contiguous
- * dimension must be at least 16-byte aligned): A, B and C must be 16-byte
- * aligned and ld * sizeof(element) must be a multiple of 16.  Each operand
- * must be readable (C: writable) over its padded extent: for A k-major,
- * (M-1)*lda elements plus K rounded up to a 16-byte multiple; likewise for
- * the other majors.  The ld padding may hold anything, NaN included: it never
- * reaches C.  C's padding is never written.
+ * dimension must be at least 16-byte aligned for its vectorised copies, and
+ * the example falls back to scalar copies otherwise).  Pointers must be
+ * aligned to their element size.  When A, B and C are 16-byte aligned and
+ * every ld * sizeof(element) (and every batch stride) is a multiple of 16,
+ * all tile configs can run and each operand must be readable (C: writable)
+ * over its padded extent: for A k-major, (M-1)*lda elements plus K rounded up
+ * to a 16-byte multiple; likewise for the other majors.  Otherwise only the
+ * element-by-element ("scalar") configs run, with any ld >= the contiguous
+ * extent, and the exact extent ((M-1)*lda + K elements for A k-major) is
+ * read.  The ld padding may hold anything, NaN included: it never reaches C.
+ * C's padding is never written.
  *
  * Asynchrony.  gemm_run only enqueues work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns.  The caller synchronises.  Launch errors
@@ -73,7 +78,8 @@ typedef enum {
     GEMM_ERR_BAD_DTYPE = 3,    /* dtype not a gemm_dtype_t                               */
     GEMM_ERR_BAD_LD = 4,       /* ld below the contiguous extent (or 1); bad batch stride */
     GEMM_ERR_NULL_PTR = 5,     /* A or B NULL while M*N*K > 0, or C NULL while M*N > 0   */
-    GEMM_ERR_MISALIGNED = 6,   /* pointer not 16-byte aligned, or ld*elem not 16-byte multiple */
+    GEMM_ERR_MISALIGNED = 6,   /* pointer not element-aligned (workspace: 16 bytes), or a
+                                  forced config that needs 16-byte alignment the operands lack */
     GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */
     GEMM_ERR_NO_CONFIG = 8,    /* config id out of range for this dtype                  */
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */

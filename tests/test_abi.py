@@ -61,14 +61,34 @@ def test_validation_errors_without_gpu():
     assert run(A=NULL) == b.GEMM_ERR_NULL_PTR
     assert run(B=NULL) == b.GEMM_ERR_NULL_PTR
     assert run(C=NULL) == b.GEMM_ERR_NULL_PTR
-    assert run(A=P + 4) == b.GEMM_ERR_MISALIGNED
-    assert run(C=3 * P + 8) == b.GEMM_ERR_MISALIGNED
-    assert run(K=30, lda=30, ldb=32) == b.GEMM_ERR_MISALIGNED   # 30 * 4 bytes
-    assert run(K=60, dtype=1, lda=60, ldb=64) == b.GEMM_ERR_MISALIGNED  # 120 bytes
+    assert run(A=P + 2) == b.GEMM_ERR_MISALIGNED               # fp32 needs 4-byte alignment
+    assert run(C=3 * P + 1, dtype=2) == b.GEMM_ERR_MISALIGNED   # bf16 C needs 2
+    assert run(B=2 * P + 1, dtype=1) == b.GEMM_ERR_MISALIGNED
     assert run(C=P + 64 * 16) == b.GEMM_ERR_ALIAS          # C starts inside A
     assert run(C=P - 64 * 64 * 4 + 16) == b.GEMM_ERR_ALIAS  # C ends inside A
     assert run(lda=63, a="x") == b.GEMM_ERR_BAD_MAJOR       # checks run in header order
     assert g.gemm_last_config() == -1
+
+
+def test_unaligned_operands_take_the_scalar_configs_without_gpu():
+    """Operands that are not 16-byte aligned pass validation (the launch then
+    fails only for lack of a GPU here) and run on the element-by-element
+    configs; a forced 16-byte config is refused."""
+    scalar = [i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i).endswith("scalar")]
+    assert len(scalar) == 2
+    for kw in (dict(K=30, lda=30, ldb=32), dict(A=P + 4), dict(C=3 * P + 8), dict(ldc=65),
+               dict(K=60, dtype=1, lda=60, ldb=64), dict(A=P + 2, dtype=2)):
+        assert run(**kw) == b.GEMM_ERR_HIP, kw
+    assert run_batched(sa=2) == b.GEMM_ERR_HIP                  # 8-byte batch stride
+    args = (64, 64, 30, "k", "k", "n", 0, P, 2 * P, 3 * P, 30, 30, 64, 0)
+    assert g.gemm_run_config(*args, 0) == b.GEMM_ERR_MISALIGNED
+    assert g.gemm_run_config(*args, scalar[0]) == b.GEMM_ERR_HIP
+    # aligned operands may use a scalar config too
+    assert g.gemm_run_config(64, 64, 64, "k", "k", "n", 0, P, 2 * P, 3 * P, 64, 64, 64, 0,
+                             scalar[1]) == b.GEMM_ERR_HIP
+    for d in range(5):
+        assert sum(g.gemm_config_describe(d, i).endswith("scalar")
+                   for i in range(g.gemm_num_configs(d))) == 2
 
 
 def test_degenerate_sizes_without_gpu():
@@ -91,8 +111,7 @@ def test_batched_validation_without_gpu():
     assert run_batched(sa=-64) == b.GEMM_ERR_BAD_LD
     assert run_batched(sc=64 * 64 - 4) == b.GEMM_ERR_BAD_LD     # C entries would overlap
     assert run_batched(sc=0) == b.GEMM_ERR_BAD_LD               # ... also when identical
-    assert run_batched(sa=2) == b.GEMM_ERR_MISALIGNED           # 8-byte stride
-    assert run_batched(sc=64 * 64 + 2) == b.GEMM_ERR_MISALIGNED
+
     # A's entries reach into C's range: entry 2 of A starts at 3P.
     assert run_batched(batch=3, sa=(1 << 20) // 4) == b.GEMM_ERR_ALIAS
     # batch 0 launches nothing and needs no pointers; strides may then be anything >= 0.

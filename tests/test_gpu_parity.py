@@ -545,3 +545,70 @@ def test_epilogue_large_direct_kernels():
         name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
         log(f"  {dtype} {layout}: {name}")
         assert name.endswith("dma"), name
+
+
+# ---------------------------------------------------------------- operands not 16-byte aligned
+
+def _upload_at(arr, off):
+    """Device copy of flat storage `arr` starting `off` elements into a fresh
+    buffer (so the pointer is only element-aligned); returns (tensor, ptr)."""
+    t = gu.to_device(np.concatenate([np.zeros(off, arr.dtype), arr, np.zeros(8, arr.dtype)]))
+    return t, t.data_ptr() + off * arr.itemsize
+
+
+def unaligned_case(M, N, K, layout, dtype, kind, pads=(1, 3, 1), offs=(1, 2, 1), config=None, seed=21):
+    """Leading dimensions extent + pads and pointers offs elements past a
+    16-byte boundary; compared with the oracle, C's padding must keep the
+    sentinel."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    a_m, b_m, c_m = layout
+    code = gi.DTYPE_CODE[dtype]
+    lda = (K if a_m == "k" else M) + pads[0]
+    ldb = (K if b_m == "k" else N) + pads[1]
+    ldc = (N if c_m == "n" else M) + pads[2]
+    prob = gi.problem(M, N, K, a_m, b_m, c_m, dtype, kind, seed=seed, lda=lda, ldb=ldb, ldc=ldc,
+                      pad_fill=float("nan"))
+    ta, pa = _upload_at(prob["A"], offs[0])
+    tb, pb = _upload_at(prob["B"], offs[1])
+    c0 = gu.c_buffer(prob).cpu().numpy()
+    tc, pc = _upload_at(c0, offs[2])
+    s = torch.cuda.current_stream()
+    args = (M, N, K, a_m, b_m, c_m, code, pa, pb, pc, lda, ldb, ldc, s.cuda_stream)
+    st = g.gemm_run(*args) if config is None else g.gemm_run_config(*args, config)
+    assert st == 0, g.gemm_status_str(st)
+    used = g.gemm_config_describe(code, g.gemm_last_config())
+    s.synchronize()
+    flat = tc.cpu().numpy()[offs[2]:offs[2] + c0.size]
+    got, flat = gu.host_c(torch.from_numpy(flat.view(np.int16) if flat.dtype == np.uint16 else flat), prob)
+    ok, info = gu.check(got, gu.reference(prob), prob, kind == "int5")
+    assert ok, (layout, dtype, used, info)
+    assert gu.padding_intact(flat, prob)
+    return used
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_unaligned_operands_every_layout(dtype):
+    """Odd leading dimensions and pointers one or two elements past a 16-byte
+    boundary (NaN in the ld padding): the element-by-element configs, chosen
+    automatically, bit-exact on integer inputs; both scalar configs forced."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    scalar = [i for i in range(g.gemm_num_configs(code)) if g.gemm_config_describe(code, i).endswith("scalar")]
+    for layout in LAYOUTS8:
+        used = unaligned_case(200, 136, 72, layout, dtype, "int5")
+        assert used.endswith("scalar"), used
+        for cfg in scalar:
+            unaligned_case(97, 65, 37, layout, dtype, "int5", pads=(3, 1, 5), offs=(3, 1, 2), config=cfg)
+    log(f"{dtype}: unaligned operands, 8 layouts")
+
+
+def test_unaligned_large_and_noninteger():
+    used = unaligned_case(2049, 1537, 515, ("k", "k", "n"), "f32", "u11")
+    assert used.startswith("f32 128x128")
+    unaligned_case(1031, 777, 300, ("m", "n", "m"), "bf16_bf16", "n002", pads=(5, 7, 9), offs=(7, 5, 3))
+
+
+def test_unaligned_aligned_pointers_odd_ld_only():
+    used = unaligned_case(300, 200, 136, ("k", "k", "n"), "f32", "int5", pads=(1, 1, 1), offs=(0, 0, 0))
+    assert used.endswith("scalar")
