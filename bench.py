@@ -15,7 +15,9 @@ The JSON line also carries:
                 problem on this host's cores, with the GPU rows compared to it;
   workloads     the other measured GEMM workloads (fp16 4096^3 in all eight
                 layouts, fp32 1024x512x256, fp32 4095x2049x1028 ragged, bf16
-                65536x256x4096 tall-skinny with its HBM GB/s).
+                65536x256x4096 tall-skinny with its HBM GB/s), and the rows
+                built on the plain GEMM: stream-K, the fused epilogue, the
+                strided-batched mode, operands that are not 16-byte aligned.
 """
 import argparse
 import hashlib
@@ -58,6 +60,26 @@ for _k in (512, 1024, 2048, 4096, 8192, 16384):
     WORKLOADS[f"fp16_sweep_k{_k}"] = (
         8192, 8192, _k, "k", "n", "n", "f16_f16", "n01", None,
         f"fp16 GEMM 8192x8192x{_k} -> fp16, A k, B n, C n, normal(0,1)")
+
+# The rows built on top of the plain GEMM, each timed on a workload of its
+# own: stream-K (persistent) scheduling on the ragged fp32 problem, the fused
+# elementwise epilogue on the headline problem, the strided-batched mode, and
+# the element-by-element path for operands that are not 16-byte aligned.
+WORKLOADS["fp32_ragged_streamk"] = WORKLOADS["fp32_ragged"][:9] + (
+    "fp32 ragged GEMM 4095x2049x1028 on the stream-K config f32 128x128x32 sk (workspace)",)
+WORKLOADS["fp32_8192_epilogue"] = WORKLOADS["fp32_8192"][:9] + (
+    "fp32 SGEMM 8192^3 (A m, B n, C n) with epilogue relu(A.B^T + bias[n])",)
+WORKLOADS["fp16_batched_64x512"] = (512, 512, 512, "k", "k", "n", "f16_f32", "n01", None,
+                                    "fp16 strided-batched GEMM, 64 x (512x512x512) -> fp32, A k, B k, C n")
+WORKLOADS["fp32_ragged_unaligned"] = WORKLOADS["fp32_ragged"][:8] + (2049,
+    "fp32 ragged GEMM 4095x2049x1028 with lda = ldb = 1029, ldc = 2049 (not 16-byte multiples)",)
+OPTIONS = {
+    "fp32_ragged_streamk": {"config": "f32 128x128x32 w2x2 mfma32 s2 dma sk"},
+    "fp32_8192_epilogue": {"epilogue": "bias_relu"},
+    "fp16_batched_64x512": {"batch": 64},
+    "fp32_ragged_unaligned": {"lda": 1029, "ldb": 1029},
+}
+NEXT_ROWS = list(OPTIONS)
 
 HEADLINE = "fp32_8192"
 
@@ -107,30 +129,55 @@ class Problem:
         import numpy as np
         import torch
 
+        import dense_gemm_engineering_run_amd as g
         import gemm_inputs as gi
         M, N, K, a, b, c, dtype, kind, ldc, desc = WORKLOADS[name]
+        opt = OPTIONS.get(name, {})
         self.name, self.desc = name, desc
-        self.p = gi.problem(M, N, K, a, b, c, dtype, kind, seed=seed, ldc=ldc)
+        self.p = gi.problem(M, N, K, a, b, c, dtype, kind, seed=seed, ldc=ldc,
+                            lda=opt.get("lda"), ldb=opt.get("ldb"))
         p = self.p
+        self.batch = opt.get("batch", 1)
 
         def dev(x):
             x = np.ascontiguousarray(x)
+            if self.batch > 1:                  # the same operand in every batch entry
+                x = np.tile(x, self.batch)
             return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
         self.a, self.b = dev(p["A"]), dev(p["B"])
         outer = N if p["c_first"] else M
         ct = torch.float32 if p["out_type"] == "f32" else torch.int16
-        self.c = torch.zeros(outer * p["ldc"], dtype=ct, device="cuda")
+        self.sc = outer * p["ldc"]
+        self.c = torch.zeros(self.sc * self.batch, dtype=ct, device="cuda")
         self.stream = torch.cuda.current_stream()
         self.args = (M, N, K, a, b, c, p["dtype"], self.a.data_ptr(), self.b.data_ptr(),
                      self.c.data_ptr(), p["lda"], p["ldb"], p["ldc"], self.stream.cuda_stream)
+        self.config = -1
+        if "config" in opt:
+            names = [g.gemm_config_describe(p["dtype"], i) for i in range(g.gemm_num_configs(p["dtype"]))]
+            self.config = names.index(opt["config"])
+        self.ws_bytes = g.gemm_workspace_size(M, N, K, a, b, c, p["dtype"], self.config)
+        self.ws = torch.zeros(max(self.ws_bytes, 16) // 4, dtype=torch.int32, device="cuda")
+        self.epi = None
+        if opt.get("epilogue") == "bias_relu":
+            self.bias = torch.linspace(-1, 1, N, device="cuda")
+            self.epi = g.Epilogue(1.0, 0.0, self.bias.data_ptr(), g.GEMM_ACT_RELU)
         eb = gi.ELEM_BYTES[p["in_type"]]
         eo = gi.ELEM_BYTES[p["out_type"]]
-        self.flops = 2.0 * M * N * K
-        self.bytes = float(M * K * eb + N * K * eb + M * N * eo)
+        self.flops = 2.0 * M * N * K * self.batch
+        self.bytes = float(M * K * eb + N * K * eb + M * N * eo) * self.batch
 
-    def launch(self):
+    def launch(self, stream=None):
         import dense_gemm_engineering_run_amd as g
-        st = g.gemm_run(*self.args)
+        args = self.args if stream is None else self.args[:-1] + (stream,)
+        if self.batch > 1:
+            st = g.gemm_run_batched(*args[:-1], self.batch, len(self.p["A"]), len(self.p["B"]),
+                                    self.sc, args[-1])
+        elif self.epi is not None or self.config >= 0 or self.ws_bytes:
+            st = g.gemm_run_ex(*args[:-1], self.epi, self.ws.data_ptr(), self.ws_bytes, args[-1],
+                               self.config)
+        else:
+            st = g.gemm_run(*args)
         if st != 0:
             raise RuntimeError(g.gemm_status_str(st))
 
@@ -163,20 +210,15 @@ class Problem:
         """Mean ms per launch when `steps` launches are captured once into a HIP
         graph and the graph is replayed (no per-launch host overhead)."""
         import torch
-
-        import dense_gemm_engineering_run_amd as g
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
             self.launch()                           # eager warm-up on the capture stream
             torch.cuda.synchronize()
-            args = self.args[:-1] + (s.cuda_stream,)
             with torch.cuda.graph(graph, stream=s):
                 for _ in range(steps):
-                    st = g.gemm_run(*args)
-                    if st != 0:
-                        raise RuntimeError(g.gemm_status_str(st))
+                    self.launch(s.cuda_stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < min_warm_s:
@@ -258,7 +300,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--others", default="all",
                     help="comma list of extra workloads to time, 'all' (the five workloads' "
-                         "others), 'sweep' (the fp16 K sweep) or 'none'")
+                         "others and the stream-K / epilogue / batched / unaligned rows), "
+                         "'sweep' (the fp16 K sweep), 'next' (those four rows) or 'none'")
     ap.add_argument("--other-steps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables it)")
@@ -331,6 +374,8 @@ def main():
         others = default_others
     elif args.others == "sweep":
         others = [w for w in WORKLOADS if w.startswith("fp16_sweep")]
+    elif args.others == "next":
+        others = NEXT_ROWS
     else:
         others = [w for w in args.others.split(",") if w]
     if others:
