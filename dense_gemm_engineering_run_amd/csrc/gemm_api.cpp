@@ -282,7 +282,11 @@ bool is_scalar(int dtype, int config)
     return config >= 0 && config < n && all[config].scalar;
 }
 
-int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
+// The tuning table's choice for this problem, among the configs `usable`
+// accepts (the first usable exact match, else the nearest usable entry within
+// a factor 2 overall), else the built-in heuristic.
+template <class Usable>
+int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, Usable usable)
 {
     std::call_once(g_env_once, load_env_table);
     {
@@ -290,7 +294,7 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
         const TuneEntry* best = nullptr;
         double best_d = 0;
         for (const TuneEntry& e : g_table) {
-            if (e.dtype != dtype || e.a != a || e.b != b || e.c != c) continue;
+            if (e.dtype != dtype || e.a != a || e.b != b || e.c != c || !usable(e.config)) continue;
             if (e.M == M && e.N == N && e.K == K) return e.config;
             double d = std::fabs(std::log2((double)std::max<int64_t>(M, 1) / std::max<int64_t>(e.M, 1))) +
                        std::fabs(std::log2((double)std::max<int64_t>(N, 1) / std::max<int64_t>(e.N, 1))) +
@@ -301,6 +305,11 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
     }
     // The kernel only sees the canonical (C n-major) problem.
     return c == 'm' ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
+}
+
+int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
+{
+    return select(dtype, a, b, c, M, N, K, [](int) { return true; });
 }
 
 thread_local int t_last_config = -1;
@@ -371,15 +380,15 @@ int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t 
                uint64_t ws_bytes, bool epi = false, bool vec16 = true)
 {
     if (!vec16) return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
-    int config = select(dtype, a, b, c, M, N, K);
-    if (is_sk(dtype, config)) {
-        int n = 0;
-        const mg::KernelEntry& e = entries(dtype, &n)[config];
-        const bool swap = c == 'm';
-        if (batch != 1 || epi || workspace_need(e, swap ? N : M, swap ? M : N, K) > ws_bytes)
-            config = swap ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
-    }
-    return config;
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    const bool swap = c == 'm';
+    auto usable = [&](int config) {
+        const mg::KernelEntry& e = all[config];
+        return e.sk_occ == 0 ||
+               (batch == 1 && !epi && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
+    };
+    return select(dtype, a, b, c, M, N, K, usable);
 }
 
 int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* ws = nullptr,

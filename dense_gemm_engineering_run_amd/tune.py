@@ -53,10 +53,18 @@ def load_log(path):
     return done
 
 
-def best_per_key(records):
+def needs_workspace(name):
+    """Stream-K configs (names ending in ' sk') run only with a workspace."""
+    return name.endswith(" sk")
+
+
+def best_per_key(records, plain=False):
+    """Fastest passing record per key (plain: among configs that need no workspace)."""
     best = {}
     for r in records:
         if not r.get("pass") or r.get("median_us") is None:
+            continue
+        if plain and needs_workspace(r["config_name"]):
             continue
         k = r["key"]
         if k not in best or r["median_us"] < best[k]["median_us"]:
@@ -64,7 +72,10 @@ def best_per_key(records):
     return best
 
 
-def write_table(path, best, header=""):
+def write_table(path, best, header="", fallback=None):
+    """One line per key with its best config; when that config needs a
+    workspace, a second line with the best config that does not (the library
+    takes the first line it can use: gemm_run has no workspace)."""
     tmp = path + ".tmp"
     with open(tmp, "w") as f:
         f.write("# dtype a_major b_major c_major M N K config  (written by tune.py)\n")
@@ -73,6 +84,9 @@ def write_table(path, best, header=""):
         for k in sorted(best):
             r = best[k]
             f.write(f"{k} {r['config_name']}   # {r['median_us']:.2f} us\n")
+            alt = (fallback or {}).get(k)
+            if needs_workspace(r["config_name"]) and alt is not None:
+                f.write(f"{k} {alt['config_name']}   # {alt['median_us']:.2f} us, no workspace\n")
     os.replace(tmp, path)
 
 
@@ -122,7 +136,7 @@ def tune(keys, measure, config_names, log_path=None, table_path=None, verbose=Tr
             logf.close()
     best = best_per_key(records)
     if table_path:
-        write_table(table_path, best, header)
+        write_table(table_path, best, header, fallback=best_per_key(records, plain=True))
     if verbose:
         for k in sorted(best):
             print(f"[tune] best {k}: {best[k]['config_name']} {best[k]['median_us']:.2f} us",

@@ -67,3 +67,31 @@ def test_no_passing_candidate_leaves_key_untuned(tmp_path):
                   verbose=False)
     assert best == {}
     assert [l for l in open(tmp_path / "t.txt") if not l.startswith("#")] == []
+
+
+def test_stream_k_winner_gets_a_fallback_line(tmp_path):
+    """A stream-K config needs a workspace that gemm_run does not have: the
+    table then also names the best config without one, and selection without
+    a workspace takes that line."""
+    key = (0, "k", "k", "n", 4095, 2049, 1028)
+    all_names = names(0)
+    sk = [i for i, nm in enumerate(all_names) if nm.endswith(" sk")]
+    plain = [i for i, nm in enumerate(all_names) if not nm.endswith(" sk")]
+    script = {i: (200.0 + i, True, i) for i in range(len(all_names))}
+    script[sk[0]] = (150.0, True, sk[0])        # the overall winner
+    script[plain[3]] = (160.0, True, plain[3])  # the best without a workspace
+    table = tmp_path / "table.txt"
+    T.tune([key], scripted(script, []), names, None, str(table), verbose=False)
+    lines = [l.split("#")[0].split() for l in open(table) if not l.startswith("#")]
+    assert [" ".join(l[7:]) for l in lines] == [all_names[sk[0]], all_names[plain[3]]]
+    try:
+        assert g.gemm_load_tuning(str(table)) == 0
+        assert g.gemm_tuning_size() == 2
+        assert g.gemm_select_config(4095, 2049, 1028, "k", "k", "n", 0) == plain[3]
+        # with a workspace the stream-K line is the one sized
+        assert g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0) == \
+            g.gemm_workspace_size(4095, 2049, 1028, "k", "k", "n", 0, sk[0]) > 0
+    finally:
+        from dense_gemm_engineering_run_amd import _binding as b
+        import os
+        g.gemm_load_tuning(b.DEFAULT_TABLE if os.path.exists(b.DEFAULT_TABLE) else None)
