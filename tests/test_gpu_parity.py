@@ -612,3 +612,46 @@ def test_unaligned_large_and_noninteger():
 def test_unaligned_aligned_pointers_odd_ld_only():
     used = unaligned_case(300, 200, 136, ("k", "k", "n"), "f32", "int5", pads=(1, 1, 1), offs=(0, 0, 0))
     assert used.endswith("scalar")
+
+
+def test_graph_capture_stream_k_and_epilogue():
+    """gemm_run_ex on a stream-K config (workspace counters reset by the
+    kernel itself, no memset) and on a plain config with an epilogue, each
+    captured once: every replay, with eager work between replays, equals the
+    oracle bit for bit."""
+    import torch
+
+    import dense_gemm_engineering_run_amd as g
+    import oracle
+    sk = [i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i).endswith(" sk")][2]
+    prob = gi.problem(600, 520, 200, "k", "k", "n", "f32", "int5", seed=33)
+    ref = gu.reference(prob)
+    a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+    bias = torch.arange(520, dtype=torch.float32, device="cuda") - 260.0
+    cases = [(sk, None, ref),
+             (-1, g.Epilogue(2.0, 0.0, bias.data_ptr(), g.GEMM_ACT_RELU),
+              oracle.epilogue_ref(ref, 2.0, 0.0, None, bias.cpu().numpy(), oracle.ACT_RELU))]
+    for cfg, epi, want in cases:
+        need = g.gemm_workspace_size(600, 520, 200, "k", "k", "n", 0, cfg)
+        assert (need > 0) == (cfg >= 0)
+        ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda")
+        c = gu.c_buffer(prob)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                assert g.gemm_run_ex(600, 520, 200, "k", "k", "n", 0, a.data_ptr(), b.data_ptr(),
+                                     c.data_ptr(), prob["lda"], prob["ldb"], prob["ldc"], epi,
+                                     ws.data_ptr(), need, s.cuda_stream, cfg) == 0
+        torch.cuda.synchronize()
+        for rep in range(4):
+            c.fill_(-1.0)                    # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got, _ = gu.host_c(c, prob)
+            ok, info = gu.check(got, want, prob, True)
+            assert ok, (cfg, rep, info)
+        if need:
+            assert int(torch.count_nonzero(ws[:256 // 4])) == 0     # counters back at zero
