@@ -655,3 +655,69 @@ def test_graph_capture_stream_k_and_epilogue():
             assert ok, (cfg, rep, info)
         if need:
             assert int(torch.count_nonzero(ws[:256 // 4])) == 0     # counters back at zero
+
+
+# ---------------------------------------------------------------- large sizes
+
+def _exact_case(M, N, K, layout, dtype, A_log, B_log, batch=1):
+    """Upload logical A (M x K) and B (N x K) in the given majors, run, and
+    compare with the exact integer product (values keep every fp32 partial
+    sum exact)."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    a_m, b_m, c_m = layout
+    code = gi.DTYPE_CODE[dtype]
+    _, tin, tout = gi.DTYPES[code]
+    lda = gi.min_ld(M if a_m == "m" else K, gi.ELEM_BYTES[tin])
+    ldb = gi.min_ld(N if b_m == "n" else K, gi.ELEM_BYTES[tin])
+    ldc = gi.min_ld(M if c_m == "m" else N, gi.ELEM_BYTES[tout])
+    A = gi.store(gi.cast(A_log, tin), a_m == "m", lda)
+    B = gi.store(gi.cast(B_log, tin), b_m == "n", ldb)
+    outer = N if c_m == "m" else M
+    a, b = gu.to_device(A), gu.to_device(B)
+    c = torch.zeros(outer * ldc * batch, dtype=torch.float32 if tout == "f32" else torch.int16, device="cuda")
+    s = torch.cuda.current_stream()
+    st = g.gemm_run_batched(M, N, K, a_m, b_m, c_m, code, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                            lda, ldb, ldc, batch, 0, 0, outer * ldc, s.cuda_stream)
+    assert st == 0, g.gemm_status_str(st)
+    s.synchronize()
+    want = A_log.astype(np.float64) @ B_log.astype(np.float64).T
+    flat = c.cpu().numpy()
+    if tout != "f32":
+        flat = flat.view(np.uint16)
+    for l in (0, batch // 2, batch - 1):
+        got = gi.load(flat[l * outer * ldc:(l + 1) * outer * ldc], M, N, c_m == "m", ldc)
+        ok, info = gu.compare.check(np.ascontiguousarray(got), want, tout, True)
+        assert ok, (l, info)
+
+
+def test_long_k_exact():
+    """K = 2^22 (a 16 MiB row per operand row): values in {-1, 0, 1} keep
+    every fp32 partial sum an exact integer."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    K = 1 << 22
+    A = rng.integers(-1, 2, size=(48, K)).astype(np.float32)
+    B = rng.integers(-1, 2, size=(40, K)).astype(np.float32)
+    log(f"long K {K}")
+    _exact_case(48, 40, K, ("k", "k", "n"), "f32", A, B)
+    _exact_case(48, 40, K, ("m", "n", "m"), "bf16_f32", A, B)
+
+
+def test_tall_m_exact():
+    """M = 2^20 rows (4096 tiles of 256 along M)."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    M = 1 << 20
+    A = rng.integers(-5, 6, size=(M, 64)).astype(np.float32)
+    B = rng.integers(-5, 6, size=(48, 64)).astype(np.float32)
+    log(f"tall M {M}")
+    _exact_case(M, 48, 64, ("k", "k", "n"), "f16_f32", A, B)
+    _exact_case(M, 48, 64, ("m", "k", "n"), "f32", A, B)
+
+
+def test_max_batch_exact():
+    """The largest batch (65535 entries on grid.y) of a broadcast 16x24x8 problem."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    A = rng.integers(-5, 6, size=(16, 8)).astype(np.float32)
+    B = rng.integers(-5, 6, size=(24, 8)).astype(np.float32)
+    log("batch 65535")
+    _exact_case(16, 24, 8, ("k", "k", "n"), "f32", A, B, batch=65535)
