@@ -1,7 +1,9 @@
 // gemm_api.cpp -- host side of the C ABI declared in include/mi355_gemm.h.
 //
 // Argument checks (all before any HIP call), the C-m-major swap, tile config
-// selection from the tuning table, and the launch.  The interface follows the
+// selection from the tuning table (stream-K configs only with a workspace,
+// element-by-element configs for operands that are not 16-byte aligned), the
+// stream-K schedule, the epilogue and batch parameters, and the launch.  The interface follows the
 // pages' problem statement: device pointers, M/N/K, per-operand majors and
 // leading dimensions, and a stream (CuTe DSL Ampere SGEMM example: docstring,
 // SGemm.__call__ and run(); CK Tile practice GEMM README, "Kernel Launch").

@@ -22,6 +22,10 @@
 // 128 bits in either layout; a 128x128 wave tile issues 64 MFMAs per step.
 // When both A and B are m/n-contiguous, a lane's 16 accumulators hold 4x4
 // blocks of C, written with 128-bit stores.
+//
+// The main loop over a range of k-tiles and the epilogue are separate pieces
+// (F32Dma), so that the persistent stream-K kernel at the end of this file can
+// run partial k-ranges of a tile.
 #pragma once
 
 #include "gemm_dma.hpp"

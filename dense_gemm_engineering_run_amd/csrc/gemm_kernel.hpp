@@ -39,7 +39,16 @@
 //  * Workgroup -> tile: workgroups are dispatched round-robin over the 8 XCDs,
 //    so the linear id is remapped to give each XCD a contiguous range of the
 //    tile order, and that order walks groups of `group_m` tile rows column by
-//    column (L2 reuse inside one XCD).
+//    column (L2 reuse inside one XCD).  grid.y indexes the entries of a
+//    strided batch.
+//  * Operands that are not 16-byte aligned use the same kernel with VEC =
+//    false: each 16-byte chunk is loaded element by element.
+//  * Epilogue: the plain store writes each accumulator; with the elementwise
+//    epilogue (act(alpha * acc + beta * C_old + bias)) the tile goes through
+//    LDS in bands and out as 4-wide runs (store_tile_via_lds).
+//
+// This header also holds what the other kernels share: Params, the buffer
+// helpers, the swizzle, the epilogue helpers and the tile raster.
 #pragma once
 
 #include <hip/hip_runtime.h>
