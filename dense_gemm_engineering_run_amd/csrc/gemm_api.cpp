@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cctype>
 #include <cmath>
 #include <cstdio>
@@ -192,6 +193,7 @@ struct TuneEntry {
 
 std::mutex g_table_mu;
 std::vector<TuneEntry> g_table;
+std::atomic<unsigned> g_table_gen{0};   // bumped whenever the table changes
 std::once_flag g_env_once;
 
 int dtype_from_name(const std::string& s)
@@ -239,6 +241,7 @@ void load_env_table()
     if (parse_table(p, t) == GEMM_OK) {
         std::lock_guard<std::mutex> g(g_table_mu);
         g_table.swap(t);
+        ++g_table_gen;
     } else {
         std::fprintf(stderr, "mi355_gemm: cannot read tuning table %s; using built-in choices\n", p);
     }
@@ -378,8 +381,8 @@ bool epi_active(const gemm_epilogue_t* epi)
 // The config gemm_run* launches when none is forced: the table's choice,
 // unless it is a stream-K config that cannot run here (batched call, an
 // epilogue, or no workspace of the size it needs), then the heuristic.
-int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
-               uint64_t ws_bytes, bool epi = false, bool vec16 = true)
+int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
+                        uint64_t ws_bytes, bool epi, bool vec16)
 {
     if (!vec16) return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
     int n = 0;
@@ -391,6 +394,33 @@ int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t 
                (batch == 1 && !epi && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
     };
     return select(dtype, a, b, c, M, N, K, usable);
+}
+
+// select_for_uncached with a one-entry memo per thread: repeated calls with
+// the same problem (the common case in a loop) skip the table scan.
+struct SelectMemo {
+    bool valid = false;
+    unsigned gen = 0;
+    int dtype = 0;
+    char a = 0, b = 0, c = 0;
+    int64_t M = 0, N = 0, K = 0, batch = 0;
+    uint64_t ws_bytes = 0;
+    bool epi = false, vec16 = false;
+    int config = -1;
+};
+thread_local SelectMemo t_memo;
+
+int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
+               uint64_t ws_bytes, bool epi = false, bool vec16 = true)
+{
+    const unsigned gen = g_table_gen.load();
+    SelectMemo& m = t_memo;
+    if (m.valid && m.gen == gen && m.dtype == dtype && m.a == a && m.b == b && m.c == c && m.M == M &&
+        m.N == N && m.K == K && m.batch == batch && m.ws_bytes == ws_bytes && m.epi == epi && m.vec16 == vec16)
+        return m.config;
+    const int config = select_for_uncached(dtype, a, b, c, M, N, K, batch, ws_bytes, epi, vec16);
+    m = SelectMemo{true, gen, dtype, a, b, c, M, N, K, batch, ws_bytes, epi, vec16, config};
+    return config;
 }
 
 int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* ws = nullptr,
@@ -619,6 +649,7 @@ int gemm_load_tuning(const char* path)
     }
     std::lock_guard<std::mutex> g(g_table_mu);
     g_table.swap(t);
+    ++g_table_gen;
     return GEMM_OK;
 }
 

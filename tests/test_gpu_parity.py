@@ -721,3 +721,50 @@ def test_max_batch_exact():
     B = rng.integers(-5, 6, size=(24, 8)).astype(np.float32)
     log("batch 65535")
     _exact_case(16, 24, 8, ("k", "k", "n"), "f32", A, B, batch=65535)
+
+
+# ---------------------------------------------------------------- seeded random sweep
+
+def test_random_shapes_configs_layouts_exact():
+    """120 seeded random cases: M, N, K in [1, 400], any layout and dtype,
+    extra leading-dimension padding (16-byte multiples or odd), a random
+    config among those the operands allow (stream-K ones with a workspace);
+    integer inputs, bit-exact against the oracle, C padding untouched."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    rng = np.random.Generator(np.random.PCG64(2024))
+    for case in range(120):
+        dtype = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"][rng.integers(5)]
+        code = gi.DTYPE_CODE[dtype]
+        M, N, K = (int(x) for x in rng.integers(1, 401, size=3))
+        a_m, b_m, c_m = LAYOUTS8[rng.integers(8)]
+        _, tin, tout = gi.DTYPES[code]
+        aligned = rng.random() < 0.7
+        def ld(inner, es):
+            base = gi.min_ld(inner, es) if aligned else inner
+            return base + (int(rng.integers(0, 3)) * (16 // es) if aligned else int(rng.integers(0, 4)))
+        lda = ld(M if a_m == "m" else K, gi.ELEM_BYTES[tin])
+        ldb = ld(N if b_m == "n" else K, gi.ELEM_BYTES[tin])
+        ldc = ld(M if c_m == "m" else N, gi.ELEM_BYTES[tout])
+        vec = all((x * e) % 16 == 0 for x, e in ((lda, gi.ELEM_BYTES[tin]), (ldb, gi.ELEM_BYTES[tin]),
+                                                   (ldc, gi.ELEM_BYTES[tout])))
+        names = [g.gemm_config_describe(code, i) for i in range(g.gemm_num_configs(code))]
+        allowed = [i for i, nm in enumerate(names) if vec or nm.endswith("scalar")]
+        cfg = int(rng.choice(allowed))
+        prob = gi.problem(M, N, K, a_m, b_m, c_m, dtype, "int5", seed=case, lda=lda, ldb=ldb, ldc=ldc,
+                          pad_fill=float("nan"))
+        need = g.gemm_workspace_size(M, N, K, a_m, b_m, c_m, code, cfg)
+        ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda")
+        a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+        c = gu.c_buffer(prob)
+        s = torch.cuda.current_stream()
+        st = g.gemm_run_ws(M, N, K, a_m, b_m, c_m, code, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                           lda, ldb, ldc, ws.data_ptr() if need else 0, need, s.cuda_stream, cfg)
+        what = (case, dtype, M, N, K, a_m + b_m + c_m, lda, ldb, ldc, names[cfg])
+        assert st == 0, (what, g.gemm_status_str(st))
+        s.synchronize()
+        got, flat = gu.host_c(c, prob)
+        ok, info = gu.check(got, gu.reference(prob), prob, True)
+        assert ok, (what, info)
+        assert gu.padding_intact(flat, prob), what
+    log("120 random cases exact")
