@@ -768,3 +768,66 @@ def test_random_shapes_configs_layouts_exact():
         assert ok, (what, info)
         assert gu.padding_intact(flat, prob), what
     log("120 random cases exact")
+
+
+# ---------------------------------------------------------------- Python helper and threads
+
+def test_torch_helper_all_layouts():
+    """gemm(a, b, c) on torch views: majors and leading dimensions come from
+    the strides (transposed views give the m/n-major storage); integer inputs,
+    exact against the fp64 product."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    rng = np.random.Generator(np.random.PCG64(8))
+    M, N, K = 150, 90, 70
+    A = rng.integers(-5, 6, size=(M, K)).astype(np.float32)
+    B = rng.integers(-5, 6, size=(N, K)).astype(np.float32)
+    want = A.astype(np.float64) @ B.astype(np.float64).T
+    for tin, tout in [(torch.float32, torch.float32), (torch.float16, torch.float32),
+                      (torch.bfloat16, torch.bfloat16)]:
+        for at, bt, ct in itertools.product([False, True], repeat=3):
+            a = torch.from_numpy(A).to(tin)
+            b = torch.from_numpy(B).to(tin)
+            a = (a.t().contiguous().cuda().t() if at else a.cuda())
+            b = (b.t().contiguous().cuda().t() if bt else b.cuda())
+            c = torch.zeros((N, M) if ct else (M, N), dtype=tout, device="cuda")
+            c = c.t() if ct else c
+            g.gemm(a, b, c)
+            torch.cuda.synchronize()
+            got = c.float().cpu().numpy().astype(np.float64)
+            want_t = torch.from_numpy(want).to(tout).double().numpy()   # exact sums, rounded to C's type
+            assert np.array_equal(got, want_t), (tin, at, bt, ct)
+
+
+def test_concurrent_host_threads():
+    """Four host threads, each on its own stream, enqueue different problems
+    through the C ABI at the same time (ctypes releases the GIL): every result
+    is exact."""
+    import threading
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    shapes = [(256, 192, 96, "f32"), (300, 200, 136, "f16_f32"), (130, 260, 72, "bf16_bf16"),
+              (512, 512, 64, "f16_f16")]
+    probs = [gi.problem(M, N, K, "k", "n", "n", dt, "int5", seed=40 + i) for i, (M, N, K, dt) in enumerate(shapes)]
+    devs = [(gu.to_device(p["A"]), gu.to_device(p["B"]), gu.c_buffer(p)) for p in probs]
+    streams = [torch.cuda.Stream() for _ in probs]
+    errors = []
+
+    def work(i):
+        p, (a, b, c), s = probs[i], devs[i], streams[i]
+        for _ in range(25):
+            st = g.gemm_run(p["M"], p["N"], p["K"], "k", "n", "n", p["dtype"], a.data_ptr(), b.data_ptr(),
+                            c.data_ptr(), p["lda"], p["ldb"], p["ldc"], s.cuda_stream)
+            if st != 0:
+                errors.append((i, st))
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(probs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for p, (a, b, c) in zip(probs, devs):
+        got, flat = gu.host_c(c, p)
+        ok, info = gu.check(got, gu.reference(p), p, True)
+        assert ok, info
