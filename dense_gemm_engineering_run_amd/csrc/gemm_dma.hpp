@@ -298,11 +298,16 @@ gemm_dma_kernel(Params p)
         for (int g = 0; g < NG; ++g) {
             __builtin_amdgcn_sched_barrier(0);
             // This k-group's share of the loads of tile t+STAGES-1 (into the stage
-            // tile t-1 used, which every wave has left at the barrier above).
-            if (more) {
-                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
-                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
-                         (g + 1) * OB::IPW / NG);
+            // tile t-1 used, which every wave has left at the barrier above),
+            // spread over the first NI k-groups: spread, so the loads do not
+            // leave in one burst after the barrier; within the first half of
+            // the tile, so that with two stages the last share still has half
+            // a tile to land (measured: 2-4 % faster than spreading over all).
+            constexpr int NI = NG < 2 ? NG : 2;
+            if (more && g < NI) {
+                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
+                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI,
+                         (g + 1) * OB::IPW / NI);
             }
             if (g + 1 < NG) read(g + 1, (g + 1) & 1);
 #pragma unroll
