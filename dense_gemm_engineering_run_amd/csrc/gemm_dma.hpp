@@ -41,8 +41,6 @@ namespace mg {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 // Workgroup barrier without a memory fence: ordering of this workgroup's LDS
 // traffic is ensured by explicit waits; the empty asm statements keep the
 // compiler from moving memory accesses across it.
@@ -53,40 +51,13 @@ __device__ __forceinline__ void bare_barrier()
     asm volatile("" ::: "memory");
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
-}
-
-__device__ __forceinline__ void wait_vmcnt_rt(int n)
-{
-    switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    case 16: wait_vmcnt<16>(); break;
-    case 20: wait_vmcnt<20>(); break;
-    case 24: wait_vmcnt<24>(); break;
-    case 32: wait_vmcnt<32>(); break;
-    case 40: wait_vmcnt<40>(); break;
-    case 48: wait_vmcnt<48>(); break;
-    default: wait_vmcnt<0>(); break;    // always safe
-    }
 }
 
 // One operand's k-tile in the LDS ring, loaded with direct-to-LDS buffer loads.
@@ -254,21 +225,22 @@ gemm_dma_kernel(Params p)
     const int kvalid_last = p.K - (nkt - 1) * BK;
     const bool ragged = kvalid_last != BK;
 
-    auto issue = [&](int t) {
-        char* st = smem + (t % STAGES) * STAGE;
-        oa.issue(p.A, p.a_bytes, p.lda, m0, t * BK, st, wave);
-        ob.issue(p.B, p.b_bytes, p.ldb, n0, t * BK, st + OA::BYTES, wave);
-    };
-
+    // Every k-tile issues the loads of tile t+STAGES-1, also past the last
+    // tile: those get an empty extent (num_records 0) and write zeros into a
+    // stage that no later tile reads.  No branch precedes each k-group's
+    // loads, and the number of loads in flight is the same for every tile.
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nkt) issue(s);
+    for (int s = 0; s < STAGES - 1; ++s) {
+        const bool live = s < nkt;
+        char* st = smem + s * STAGE;
+        oa.issue(p.A, live ? p.a_bytes : 0, p.lda, m0, s * BK, st, wave);
+        ob.issue(p.B, live ? p.b_bytes : 0, p.ldb, n0, s * BK, st + OA::BYTES, wave);
+    }
 
     for (int t = 0; t < nkt; ++t) {
-        // Tile t has landed once at most min(STAGES-2, nkt-1-t) later tiles are outstanding.
-        const int later = min(STAGES - 2, nkt - 1 - t);
-        if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
-        else wait_vmcnt_rt(LPT * later);
+        // Tile t has landed once the STAGES-2 later tiles' loads are all that
+        // remain outstanding.
+        wait_vmcnt<LPT * (STAGES - 2)>();
         char* st = smem + (t % STAGES) * STAGE;
         if (t == nkt - 1 && ragged && (AK || BKM)) {
             bare_barrier();
@@ -281,6 +253,7 @@ gemm_dma_kernel(Params p)
         // __syncthreads() would also wait for the later tiles still in flight.
         bare_barrier();
         const bool more = t + STAGES - 1 < nkt;
+        const uint64_t na = more ? p.a_bytes : 0, nb = more ? p.b_bytes : 0;
         char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
         const int nk0 = (t + STAGES - 1) * BK;
 
@@ -304,9 +277,9 @@ gemm_dma_kernel(Params p)
             // the tile, so that with two stages the last share still has half
             // a tile to land (measured: 2-4 % faster than spreading over all).
             constexpr int NI = NG < 2 ? NG : 2;
-            if (more && g < NI) {
-                oa.issue(p.A, p.a_bytes, p.lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
-                ob.issue(p.B, p.b_bytes, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI,
+            if (g < NI) {
+                oa.issue(p.A, na, p.lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
+                ob.issue(p.B, nb, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI,
                          (g + 1) * OB::IPW / NI);
             }
             if (g + 1 < NG) read(g + 1, (g + 1) & 1);
@@ -318,6 +291,7 @@ gemm_dma_kernel(Params p)
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vmcnt<0>();   // the empty loads past the last tile have landed too
 
     // Epilogue (as in gemm_kernel): fp32 accumulators -> output type, predicated stores.
     if (TO == Out::F32 ? p.epi : EPI) {

@@ -191,20 +191,26 @@ struct F32Dma {
         const int64_t lda = p.lda, ldb = p.ldb;
         const bool ragged = kvalid_last != BK;
 
+        // Every k-tile issues the loads of the tile STAGES-1 ahead, also past the
+        // end of the range: those get an empty extent (num_records 0), so they
+        // write zeros into a stage that no later tile reads.  The steady state
+        // then has no branch before each step's loads (a run-time test there
+        // costs a branch and the compare feeding it between MFMA runs,
+        // measured at 2 % of the loop time), and the number of loads in flight
+        // is the same for every tile.
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s) {
-            if (kt0 + s < kt1) {
-                char* st = smem + s * STAGE;
-                oa.issue(A, a_bytes, lda, m0, (kt0 + s) * BK, st, wave);
-                ob.issue(B, b_bytes, ldb, n0, (kt0 + s) * BK, st + OA::BYTES, wave);
-            }
+            const bool live = kt0 + s < kt1;
+            char* st = smem + s * STAGE;
+            oa.issue(A, live ? a_bytes : 0, lda, m0, (kt0 + s) * BK, st, wave);
+            ob.issue(B, live ? b_bytes : 0, ldb, n0, (kt0 + s) * BK, st + OA::BYTES, wave);
         }
 
         for (int t = kt0; t < kt1; ++t) {
             const int r = t - kt0;
-            const int later = min(STAGES - 2, kt1 - 1 - t);
-            if (later == STAGES - 2) wait_vmcnt<LPT * (STAGES - 2)>();
-            else wait_vmcnt_rt(LPT * later);
+            // Tile t has landed once the STAGES-2 later tiles' loads are all
+            // that remain outstanding.
+            wait_vmcnt<LPT * (STAGES - 2)>();
             char* st = smem + (r % STAGES) * STAGE;
             if (t == nkt - 1 && ragged && (AK || BKM)) {
                 bare_barrier();
@@ -214,6 +220,7 @@ struct F32Dma {
             }
             bare_barrier();
             const bool more = t + STAGES - 1 < kt1;
+            const uint64_t na = more ? a_bytes : 0, nb = more ? b_bytes : 0;
             char* nst = smem + ((r + STAGES - 1) % STAGES) * STAGE;
             const int nk0 = (t + STAGES - 1) * BK;
             const char* sa = st;
@@ -264,11 +271,8 @@ struct F32Dma {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 __builtin_amdgcn_sched_barrier(0);
-                if (more) {
-                    oa.issue(A, a_bytes, lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
-                    ob.issue(B, b_bytes, ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG,
-                             (g + 1) * OB::IPW / NG);
-                }
+                oa.issue(A, na, lda, m0, nk0, nst, wave, g * OA::IPW / NG, (g + 1) * OA::IPW / NG);
+                ob.issue(B, nb, ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NG, (g + 1) * OB::IPW / NG);
                 if (g + 1 < NG) read(g + 1, (g + 1) & 1);
                 const int b = g & 1;
 #pragma unroll
@@ -283,6 +287,7 @@ struct F32Dma {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        wait_vmcnt<0>();   // the empty loads past the range have landed too
     }
 
     // Store the C tile at (m0, n0).  D row r of unit u maps to tile row
