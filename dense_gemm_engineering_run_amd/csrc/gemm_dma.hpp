@@ -204,7 +204,9 @@ gemm_dma_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
     select_batch(p);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index as a wave-uniform (scalar) value: the LDS addresses of the
+    // direct loads (M0) then need no v_readfirstlane per load.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
     tile_coords(p, tm, tn);

@@ -387,7 +387,9 @@ gemm_f32dma_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
 
     select_batch(p);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index as a wave-uniform (scalar) value: the LDS addresses of the
+    // direct loads (M0) then need no v_readfirstlane per load.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -439,7 +441,7 @@ gemm_f32dma_sk_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
     __shared__ int arrived;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = p.grid;
     const int xcd = blockIdx.x % 8, rank = blockIdx.x / 8;
     const int g = xcd * (G / 8) + rank;
