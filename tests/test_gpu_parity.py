@@ -143,6 +143,42 @@ def test_every_config_every_layout(dtype):
         log(f"{name}: 8 layouts exact")
 
 
+def _config_shape(name):
+    """(BK, stages) from a config description such as
+    'f16_f32 256x256x64 w4x2 mfma32 s2 dma'."""
+    import re
+    m = re.search(r"\d+x\d+x(\d+) w\dx\d mfma\d+ s(\d+)", name)
+    assert m, name
+    return int(m.group(1)), int(m.group(2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_every_config_pipeline_depths(dtype):
+    """K giving 1, 2, STAGES-1, STAGES and STAGES+1 k-tiles, each with a
+    partial last tile, for every config: the load ring's prologue and tail
+    (including loads issued past the last k-tile, which must read nothing
+    and disturb nothing) at every depth the config can reach."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    count = 0
+    for cfg in range(g.gemm_num_configs(code)):
+        name = g.gemm_config_describe(code, cfg)
+        bk, stages = _config_shape(name)
+        tiles = sorted({1, 2, max(stages - 1, 1), stages, stages + 1})
+        ks = sorted({max(1, (t - 1) * bk + (bk // 2 + 1)) for t in tiles} | {1, bk})
+        for K in ks:
+            for am, bm, cm in [(a, b, "n") for a in "km" for b in "kn"]:
+                prob = gi.problem(130, 70, K, am, bm, cm, dtype, "int5", seed=cfg * 131 + K,
+                                  pad_fill=float("nan"))
+                c, flat, st = gu.run(prob, config=cfg)
+                assert st == 0, (name, K, am, bm)
+                ok, info = gu.check(c, gu.reference(prob), prob, exact=True)
+                assert ok, (name, K, am, bm, info)
+                assert gu.padding_intact(flat, prob), (name, K, am, bm)
+                count += 1
+    log(f"{dtype}: {count} pipeline-depth cases exact")
+
+
 def test_every_config_nonintegers_multi_tile():
     import dense_gemm_engineering_run_amd as g
     for dtype, kind in [("f32", "u11"), ("f16_f32", "n01"), ("bf16_bf16", "n002")]:
