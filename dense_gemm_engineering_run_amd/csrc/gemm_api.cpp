@@ -365,11 +365,12 @@ uint64_t workspace_need(const mg::KernelEntry& e, int64_t M, int64_t N, int64_t 
     return sk_plan(e, tiles, (K + e.BK - 1) / e.BK).bytes;
 }
 
-bool is_sk(int dtype, int config)
+// A stream-K config that cannot run an active epilogue (sk_epilogue_ok).
+bool sk_without_epilogue(int dtype, int config)
 {
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
-    return config >= 0 && config < n && all[config].sk_occ > 0;
+    return config >= 0 && config < n && all[config].sk_occ > 0 && !mg::sk_epilogue_ok(all[config].BM, all[config].BN);
 }
 
 // True when the epilogue does something (else the plain store runs).
@@ -390,8 +391,8 @@ int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N,
     const bool swap = c == 'm';
     auto usable = [&](int config) {
         const mg::KernelEntry& e = all[config];
-        return e.sk_occ == 0 ||
-               (batch == 1 && !epi && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
+        return e.sk_occ == 0 || (batch == 1 && (!epi || mg::sk_epilogue_ok(e.BM, e.BN)) &&
+                                 workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
     };
     return select(dtype, a, b, c, M, N, K, usable);
 }
@@ -504,7 +505,7 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
         if (!vec16 && !is_scalar(dtype, config)) return GEMM_ERR_MISALIGNED;   // needs 16-byte loads
     }
     if (epi && (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)) return GEMM_ERR_BAD_EPILOGUE;
-    if (epi_active(epi) && is_sk(dtype, config)) return GEMM_ERR_BAD_EPILOGUE;   // stream-K: no epilogue
+    if (epi_active(epi) && sk_without_epilogue(dtype, config)) return GEMM_ERR_BAD_EPILOGUE;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc, vec16);
     x.batch = batch;
@@ -601,7 +602,7 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_HIP: return "HIP runtime error at launch";
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
     case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
-    case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation";
+    case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation, or an epilogue on a config without one";
     default: return "unknown status";
     }
 }

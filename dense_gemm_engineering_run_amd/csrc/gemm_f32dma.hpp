@@ -491,7 +491,8 @@ gemm_f32dma_sk_kernel(Params p)
         KT::zero(acc);
         KT::mainloop(p, smem, oa, ob, m0, n0, kt0, kt1, acc, tid, lane, wave);
         if (kt0 == 0 && kt1 == nkt) {
-            KT::template store<false, false>(p, m0, n0, acc, lane, wave);
+            if constexpr (sk_epilogue_ok(BM, BN)) KT::template store<false, true>(p, m0, n0, acc, lane, wave, smem);
+            else KT::template store<false, false>(p, m0, n0, acc, lane, wave);
         } else {
             const int ts = s * nkt;
             const int gf = owner(ts), gl = owner(ts + nkt - 1);
@@ -538,16 +539,7 @@ gemm_f32dma_sk_kernel(Params p)
                     for (int u = 0; u < U; ++u) {
                         const int idx = tid + (b + u) * KT::NT;
                         const int m = m0 + idx / (BN / 4), n = n0 + (idx % (BN / 4)) * 4;
-                        if (m < p.M) {
-                            float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
-                            if (n + 3 < p.N) {
-                                *(f32x4*)dst = sum[u];
-                            } else {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    if (n + e < p.N) dst[e] = sum[u][e];
-                            }
-                        }
+                        if (m < p.M) store4<TO>(p, m, n, sum[u]);   // the elementwise epilogue, if any
                     }
                 }
                 if (tid == 0) __hip_atomic_store(p.sk_count + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -750,6 +750,13 @@ gemm_kernel(Params p)
 // One tile configuration, instantiated for the four operand layouts.
 using LaunchFn = hipError_t (*)(int layout, const Params& p, hipStream_t s);
 
+// Whether a stream-K config runs the elementwise epilogue on the tiles it
+// completes in one range (staged through LDS as in the other kernels): the
+// 256x256 stream-K kernels have no registers left for it (their accumulators
+// take 256 per lane), so only smaller tiles do.  Tiles finished by the
+// reduction of partials always could; the rule is per config.
+constexpr bool sk_epilogue_ok(int BM, int BN) { return BM * BN <= 128 * 128; }
+
 struct KernelEntry {
     const char* name;
     int BM, BN, BK, WM, WN, MI;

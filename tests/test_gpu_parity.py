@@ -547,11 +547,27 @@ def test_epilogue_every_config_exact(dtype):
     code = gi.DTYPE_CODE[dtype]
     for cfg in range(g.gemm_num_configs(code)):
         name = g.gemm_config_describe(code, cfg)
-        expect = g.GEMM_ERR_BAD_EPILOGUE if name.endswith(" sk") else 0   # stream-K: no epilogue
+        # 256x256 stream-K kernels have no registers for the epilogue
+        expect = g.GEMM_ERR_BAD_EPILOGUE if name.endswith(" sk") and " 256x256x" in name else 0
         for layout in [("k", "k", "n"), ("m", "n", "m")]:
             epi_case(300, 200, 136, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg,
                      expect=expect)
         log(f"{name}: epilogue exact" if not expect else f"{name}: epilogue refused")
+
+
+def test_epilogue_stream_k_ragged():
+    """The ragged fp32 workload with an epilogue: the 128x128 stream-K config
+    runs 512 whole tiles through the staged epilogue and 32 split tiles
+    through the reduction's, bit-exact on integer inputs; with a workspace and
+    no forced config the table's stream-K choice is taken."""
+    import dense_gemm_engineering_run_amd as g
+    sk = next(i for i in range(g.gemm_num_configs(0))
+              if g.gemm_config_describe(0, i) == "f32 128x128x32 w2x2 mfma32 s2 dma sk")
+    for config in (sk, None):
+        used = epi_case(4095, 2049, 1028, ("k", "k", "n"), "f32", "int5", 2.0, -0.5, g.GEMM_ACT_RELU,
+                        config=config, seed=21)
+        assert used == sk, g.gemm_config_describe(0, used)
+    log("ragged 4095x2049x1028 with epilogue on stream-K: exact")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
@@ -652,9 +668,9 @@ def test_unaligned_aligned_pointers_odd_ld_only():
 
 def test_graph_capture_stream_k_and_epilogue():
     """gemm_run_ex on a stream-K config (workspace counters reset by the
-    kernel itself, no memset) and on a plain config with an epilogue, each
-    captured once: every replay, with eager work between replays, equals the
-    oracle bit for bit."""
+    kernel itself, no memset), on a plain config with an epilogue and on the
+    stream-K config with the epilogue, each captured once: every replay, with
+    eager work between replays, equals the oracle bit for bit."""
     import torch
 
     import dense_gemm_engineering_run_amd as g
@@ -664,9 +680,9 @@ def test_graph_capture_stream_k_and_epilogue():
     ref = gu.reference(prob)
     a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
     bias = torch.arange(520, dtype=torch.float32, device="cuda") - 260.0
-    cases = [(sk, None, ref),
-             (-1, g.Epilogue(2.0, 0.0, bias.data_ptr(), g.GEMM_ACT_RELU),
-              oracle.epilogue_ref(ref, 2.0, 0.0, None, bias.cpu().numpy(), oracle.ACT_RELU))]
+    want_epi = oracle.epilogue_ref(ref, 2.0, 0.0, None, bias.cpu().numpy(), oracle.ACT_RELU)
+    relu = g.Epilogue(2.0, 0.0, bias.data_ptr(), g.GEMM_ACT_RELU)
+    cases = [(sk, None, ref), (-1, relu, want_epi), (sk, relu, want_epi)]
     for cfg, epi, want in cases:
         need = g.gemm_workspace_size(600, 520, 200, "k", "k", "n", 0, cfg)
         assert (need > 0) == (cfg >= 0)
