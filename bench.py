@@ -63,12 +63,15 @@ for _k in (512, 1024, 2048, 4096, 8192, 16384):
 
 # The rows built on top of the plain GEMM, each timed on a workload of its
 # own: stream-K (persistent) scheduling on the ragged fp32 problem, the fused
-# elementwise epilogue on the headline problem, the strided-batched mode, and
+# elementwise epilogue on the headline problem and on stream-K, the
+# strided-batched mode, and
 # the element-by-element path for operands that are not 16-byte aligned.
 WORKLOADS["fp32_ragged_streamk"] = WORKLOADS["fp32_ragged"][:9] + (
     "fp32 ragged GEMM 4095x2049x1028 on the stream-K config f32 128x128x32 sk (workspace)",)
 WORKLOADS["fp32_8192_epilogue"] = WORKLOADS["fp32_8192"][:9] + (
     "fp32 SGEMM 8192^3 (A m, B n, C n) with epilogue relu(A.B^T + bias[n])",)
+WORKLOADS["fp32_ragged_streamk_epilogue"] = WORKLOADS["fp32_ragged"][:9] + (
+    "fp32 ragged GEMM 4095x2049x1028 on the stream-K config f32 128x128x32 sk with epilogue relu(A.B^T + bias[n])",)
 WORKLOADS["fp16_batched_64x512"] = (512, 512, 512, "k", "k", "n", "f16_f32", "n01", None,
                                     "fp16 strided-batched GEMM, 64 x (512x512x512) -> fp32, A k, B k, C n")
 WORKLOADS["fp32_ragged_unaligned"] = WORKLOADS["fp32_ragged"][:8] + (2049,
@@ -76,6 +79,7 @@ WORKLOADS["fp32_ragged_unaligned"] = WORKLOADS["fp32_ragged"][:8] + (2049,
 OPTIONS = {
     "fp32_ragged_streamk": {"config": "f32 128x128x32 w2x2 mfma32 s2 dma sk"},
     "fp32_8192_epilogue": {"epilogue": "bias_relu"},
+    "fp32_ragged_streamk_epilogue": {"config": "f32 128x128x32 w2x2 mfma32 s2 dma sk", "epilogue": "bias_relu"},
     "fp16_batched_64x512": {"batch": 64},
     "fp32_ragged_unaligned": {"lda": 1029, "ldb": 1029},
 }
