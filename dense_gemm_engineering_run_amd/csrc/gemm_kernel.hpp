@@ -413,18 +413,42 @@ __device__ __forceinline__ void store_epi(const Params& p, int m, int n, float v
 
 // Store 4 consecutive outputs (m, n .. n+3) of the canonical C, given in fp32:
 // through the elementwise epilogue when p.epi is set, then converted; one
-// 128-bit (fp32) or 64-bit (16-bit) store when all four are inside C.
+// 128-bit (fp32) or 64-bit (16-bit) store (and, for the epilogue, one load of
+// the old values) when all four are inside C and C allows it.
 template <Out TO>
 __device__ __forceinline__ void store4(const Params& p, int m, int n, f32x4 v)
 {
-    if (p.epi) {
-#pragma unroll 1
-        for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) store_epi<TO>(p, m, n + e, v[e]);
-        return;
-    }
     const int64_t idx = (int64_t)m * p.ldc + n;
-    if (p.c_vec && n + 3 < p.N) {
+    const bool whole = p.c_vec && n + 3 < p.N;
+    if (p.epi) {
+        if (!whole) {
+#pragma unroll 1
+            for (int e = 0; e < 4; ++e)
+                if (n + e < p.N) store_epi<TO>(p, m, n + e, v[e]);
+            return;
+        }
+        // All four inside C: the epilogue on the four values (the operations
+        // and their order of epi_value), then one vector store below.
+        f32x4 old = {0.f, 0.f, 0.f, 0.f};
+        if (p.beta != 0.f) {
+            if constexpr (TO == Out::F32) {
+                old = *(const f32x4*)((const float*)p.C + idx);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) old[e] = load_out<TO>(p.C, idx + e);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = p.alpha * v[e];
+            if (p.beta != 0.f) t = __builtin_fmaf(p.beta, old[e], t);
+            if (p.bias) t += p.bias[p.bias_rows ? m : n + e];
+            if (p.act == kActRelu) t = t < 0.f ? 0.f : t;
+            else if (p.act == kActGelu) t = 0.5f * t * (1.f + erf_as(t * 0.70710678118654752f));
+            v[e] = t;
+        }
+    }
+    if (whole) {
         if constexpr (TO == Out::F32) {
             *(f32x4*)((float*)p.C + idx) = v;
         } else {
