@@ -248,7 +248,7 @@ void load_env_table()
 }
 
 // Built-in choice when the table has nothing for this dtype and layout.
-int heuristic(int dtype, int64_t M, int64_t N, int64_t K)
+int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_kmajor, int64_t batch)
 {
     (void)K;
     auto pick = [&](const char* tile) {
@@ -256,17 +256,24 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K)
         int id = find_config(dtype, name);
         return id < 0 ? 0 : id;
     };
-    // Large problems (at least a full wave of 256x256 tiles) go to the
-    // direct-to-LDS kernels; smaller ones to tiles that still fill the 256 CUs.
-    const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0);
+    // Thresholds from a tuner sweep (M = N = 1024 .. 8192, K = 1024 and
+    // 4096, every dtype, operands k-major or m/n-major, one MI355X): large
+    // problems (at least a wave of 256x256 tiles) go to the direct-to-LDS
+    // 256x256 kernels, mid-size ones to 128x128 direct-to-LDS tiles, small
+    // ones to register-staged 64x64 tiles -- except 16-bit problems with an
+    // m/n-contiguous operand, whose transposing LDS reads make the 128x128
+    // direct-to-LDS tile up to 1.8x faster even there.  A strided batch
+    // counts all its entries' tiles (64 x 512^3 fp16: the 256x256 tile runs
+    // at 507 TF/s, the 64x64 one at 296).
+    const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0) * (double)std::max<int64_t>(batch, 1);
     if (dtype == GEMM_DTYPE_F32) {
         if (tiles256 >= 256) return pick("256x256x32 w2x2 mfma32 s2 dma");
-        if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 swz");
-        return pick("64x64x16 w2x2 mfma16 s2 swz");
+        if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 dma");
+        return pick("64x64x64 w2x2 mfma16 s2 swz");
     }
-    if (tiles256 >= 192) return pick("256x256x64 w2x2 mfma32 s2 dma");
+    if (tiles256 >= 192) return pick("256x256x64 w4x2 mfma32 s2 dma");
     if (tiles256 >= 64) return pick("128x128x64 w2x2 mfma32 s4 dma");
-    if (M * N >= 512 * 512) return pick("128x128x64 w2x2 mfma32 s2 swz");
+    if (tiles256 >= 16 && !(a_kmajor && b_kmajor)) return pick("128x128x64 w2x2 mfma32 s4 dma");
     return pick("64x64x64 w2x2 mfma16 s2 swz");
 }
 
@@ -289,12 +296,13 @@ bool is_scalar(int dtype, int config)
 
 // The tuning table's choice for this problem, among the configs `usable`
 // accepts (the first usable exact match, else the nearest usable entry within
-// a factor 2 overall), else the built-in heuristic.
+// a factor 2 overall), else the built-in heuristic.  The table is tuned on
+// single GEMMs, so a strided batch (batch > 1) goes to the heuristic.
 template <class Usable>
-int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, Usable usable)
+int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch, Usable usable)
 {
     std::call_once(g_env_once, load_env_table);
-    {
+    if (batch <= 1) {
         std::lock_guard<std::mutex> g(g_table_mu);
         const TuneEntry* best = nullptr;
         double best_d = 0;
@@ -308,13 +316,15 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, U
         }
         if (best && best_d <= 1.0) return best->config;   // within a factor 2 overall
     }
-    // The kernel only sees the canonical (C n-major) problem.
-    return c == 'm' ? heuristic(dtype, N, M, K) : heuristic(dtype, M, N, K);
+    // The kernel only sees the canonical (C n-major) problem: for C m-major
+    // the operands and sizes swap.
+    return c == 'm' ? heuristic(dtype, N, M, K, b == 'k', a == 'k', batch)
+                    : heuristic(dtype, M, N, K, a == 'k', b == 'k', batch);
 }
 
 int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
 {
-    return select(dtype, a, b, c, M, N, K, [](int) { return true; });
+    return select(dtype, a, b, c, M, N, K, 1, [](int) { return true; });
 }
 
 thread_local int t_last_config = -1;
@@ -394,7 +404,7 @@ int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N,
         return e.sk_occ == 0 || (batch == 1 && (!epi || mg::sk_epilogue_ok(e.BM, e.BN)) &&
                                  workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
     };
-    return select(dtype, a, b, c, M, N, K, usable);
+    return select(dtype, a, b, c, M, N, K, batch, usable);
 }
 
 // select_for_uncached with a one-entry memo per thread: repeated calls with

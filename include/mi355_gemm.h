@@ -130,12 +130,16 @@ int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c
  * Strided batched form: for l < batch, C_l = A_l * B_l^T with
  * A_l = A + l*stride_a, B_l = B + l*stride_b, C_l = C + l*stride_c (strides in
  * elements).  This is the "L" mode of the CuTe DSL Ampere SGEMM example, whose
- * run() documents an (M, N, K, L) problem size.  Strides must be >= 0 and
- * their byte sizes multiples of 16; stride_a or stride_b may be 0 (the same
+ * run() documents an (M, N, K, L) problem size.  Strides must be >= 0
+ * (strides that are not 16-byte multiples select the element-by-element
+ * configs, as unaligned pointers do); stride_a or stride_b may be 0 (the same
  * operand for every entry); C entries must not overlap (stride_c covers one
  * C, else GEMM_ERR_BAD_LD); batch <= 65535 (else GEMM_ERR_BAD_SHAPE); batch
  * == 0 launches nothing.  Aliasing is checked over the whole range each
- * operand spans.  gemm_run is the batch == 1 case.
+ * operand spans.  One launch covers every entry, so the tile config is chosen
+ * by the built-in heuristic from the tile count of all entries together (the
+ * tuning table holds single GEMMs and is not consulted).  gemm_run is the
+ * batch == 1 case.
  */
 int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                      int dtype, const void* A, const void* B, void* C,
