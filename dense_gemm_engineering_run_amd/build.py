@@ -6,7 +6,7 @@ Packed-fp32 instructions are disabled for all device code.  The build fails if
 a kernel spills more than SPILL_LIMIT bytes per lane to scratch memory (the
 compiler's resource-usage remarks are checked): accumulators spilled around a
 GEMM main loop cost several times its runtime.  The limit admits the few
-values (up to 8) that the plain 16-bit-output epilogues of the 256x256 tiles
+values (up to 9) that the plain 16-bit-output epilogues of the 256x256 tiles
 park in scratch at the loop exit, which cost nothing measurable.
 """
 import glob
@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libmi355_gemm.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SPILL_LIMIT = 32        # bytes of scratch per lane
+SPILL_LIMIT = 40        # bytes of scratch per lane
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wno-inline-asm",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

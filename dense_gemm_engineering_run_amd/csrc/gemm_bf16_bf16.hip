@@ -1,5 +1,5 @@
 // Kernel instantiations for dtype bf16_bf16 (inputs BF16, output BF16).
-#include "gemm_dma.hpp"
+#include "gemm_streamk.hpp"
 #include "configs.def"
 
 namespace mg {
@@ -14,11 +14,17 @@ namespace mg {
      BM, BN, BK, WM, WN, MI, true,                                                  \
      &DmaInst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, ST>::launch, ST, true},
 
+#define MG_DMA_SK_ENTRY(BM, BN, BK, WM, WN, MI, ST, OCC)                              \
+    {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s" #ST " dma sk",       \
+     BM, BN, BK, WM, WN, MI, true,                                                  \
+     &Dma16SkInst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, ST>::launch, ST, true, OCC},
+
 #define MG_SCALAR_ENTRY(BM, BN, BK, WM, WN, MI)                                        \
     {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2 swz scalar",              \
      BM, BN, BK, WM, WN, MI, true, &Inst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, true, false>::launch, 2, false, 0, true},
 
 static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)
+                                           MG_DMA_SK_CONFIGS_16(MG_DMA_SK_ENTRY)
                                            MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)};
 
 const KernelEntry* entries_bf16_bf16(int* n)

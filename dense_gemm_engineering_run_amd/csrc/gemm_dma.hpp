@@ -180,57 +180,257 @@ struct DmaOperand {
     }
 };
 
+// The pieces of the kernel: the main loop over a range of k-tiles of one C
+// tile, and the ways to store the tile (so that the persistent stream-K
+// kernel can run partial k-ranges with the same loop).
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM>
+struct Dma16 {
+    static_assert(TI != In::F32, "direct-to-LDS kernel is for 16-bit inputs");
+    static constexpr int TILE_M = BM, TILE_N = BN, TILE_K = BK;
+    static constexpr Out OUT = TO;
+    static constexpr int NW = WM * WN, NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / MI, TN = WTN / MI;
+    static constexpr int KG = MI == 32 ? 16 : 32;      // k per MFMA
+    static constexpr int NG = BK / KG;                 // k-groups per tile
+    static constexpr int R = MI == 32 ? 16 : 4;        // accumulators per MFMA tile and lane
+    using OA = DmaOperand<BM, BK, NW, AK>;
+    using OB = DmaOperand<BN, BK, NW, BKM>;
+    static constexpr int STAGE = OA::BYTES + OB::BYTES;
+    static constexpr int LPT = OA::IPW + OB::IPW;      // loads per wave per tile
+    static constexpr int SMEM = STAGES * STAGE;
+    static_assert(BK % KG == 0, "BK must be a multiple of the MFMA k");
+    static_assert(STAGES >= 2 && SMEM <= 160 * 1024, "LDS budget");
+    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
+    using AccT = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+    typedef AccT Acc[TM][TN];
+    static constexpr int PART_BYTES = BM * BN * 4;     // one partial tile, fp32 row-major
+
+    __device__ static __forceinline__ void zero(Acc& acc)
+    {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = AccT{};
+    }
+
+    // Tile-local row and column of accumulator q of MFMA tile (i, j).
+    __device__ static __forceinline__ int row(int wm, int i, int q, int lane)
+    {
+        return wm * WTM + i * MI + (MI == 32 ? (q / 4) * 8 + (lane / 32) * 4 + (q % 4) : (lane / 16) * 4 + q);
+    }
+    __device__ static __forceinline__ int col(int wn, int j, int lane) { return wn * WTN + j * MI + (lane % MI); }
+
+    // Accumulate k-tiles [kt0, kt1) of the C tile at (m0, n0) into acc.  The
+    // LDS ring must be free on entry (no wave still reading it); on return
+    // every load has landed.  gemm_dma_kernel writes the same loop out for the
+    // whole k-range (see there why); the two must stay in step.
+    __device__ static __forceinline__ void mainloop(const Params& p, char* smem, OA& oa, OB& ob, int m0, int n0,
+                                                    int kt0, int kt1, Acc& acc, int tid, int lane, int wave)
+    {
+        const int wm = wave / WN, wn = wave % WN;
+        const int nkt = (p.K + BK - 1) / BK;
+        const int kvalid_last = p.K - (nkt - 1) * BK;
+        const bool ragged = kvalid_last != BK;
+        // Operand fields as locals (the DMA asm statements clobber memory).
+        const char* const A = p.A;
+        const char* const B = p.B;
+        const uint64_t a_bytes = p.a_bytes, b_bytes = p.b_bytes;
+        const int64_t lda = p.lda, ldb = p.ldb;
+
+        // Every k-tile issues the loads of the tile STAGES-1 ahead, also past
+        // the end of the range: those get an empty extent (num_records 0)
+        // and write zeros into a stage that no later tile reads.  No branch
+        // precedes each k-group's loads, and the number of loads in flight is
+        // the same for every tile.
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) {
+            const bool live = kt0 + s < kt1;
+            char* st = smem + s * STAGE;
+            oa.issue(A, live ? a_bytes : 0, lda, m0, (kt0 + s) * BK, st, wave);
+            ob.issue(B, live ? b_bytes : 0, ldb, n0, (kt0 + s) * BK, st + OA::BYTES, wave);
+        }
+
+        for (int t = kt0; t < kt1; ++t) {
+            const int r = t - kt0;
+            // Tile t has landed once the STAGES-2 later tiles' loads are all
+            // that remain outstanding.
+            wait_vmcnt<LPT * (STAGES - 2)>();
+            char* st = smem + (r % STAGES) * STAGE;
+            if (t == nkt - 1 && ragged && (AK || BKM)) {
+                bare_barrier();
+                oa.template zero_tail<NT>(st, kvalid_last, tid);
+                ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
+            }
+            // A bare barrier: this wave's loads of tile t are complete (the vmcnt
+            // wait above), so after it every wave's part of tile t is in LDS.  A
+            // fenced __syncthreads() would also wait for the later tiles still in
+            // flight.
+            bare_barrier();
+            const bool more = t + STAGES - 1 < kt1;
+            const uint64_t na = more ? a_bytes : 0, nb = more ? b_bytes : 0;
+            char* nst = smem + ((r + STAGES - 1) % STAGES) * STAGE;
+            const int nk0 = (t + STAGES - 1) * BK;
+
+            const char* sa = st;
+            const char* sb = st + OA::BYTES;
+            i32x4 fa[2][TM], fb[2][TN];
+            auto read = [&](int g, int buf) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[buf][i] = oa.template frag<MI>(sa, wm * WTM + i * MI, g * KG, lane);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[buf][j] = ob.template frag<MI>(sb, wn * WTN + j * MI, g * KG, lane);
+            };
+            read(0, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                // This k-group's share of the loads of tile t+STAGES-1 (into the
+                // stage tile t-1 used, which every wave has left at the barrier
+                // above), spread over the first NI k-groups: spread, so the loads
+                // do not leave in one burst after the barrier; within the first
+                // half of the tile, so that with two stages the last share still
+                // has half a tile to land (measured: 2-4 % faster than spreading
+                // over all).
+                constexpr int NI = NG < 2 ? NG : 2;
+                if (g < NI) {
+                    oa.issue(A, na, lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
+                    ob.issue(B, nb, ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI, (g + 1) * OB::IPW / NI);
+                }
+                if (g + 1 < NG) read(g + 1, (g + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) mfma_step<TI, MI>(fa[g & 1][i], fb[g & 1][j], acc[i][j]);
+                if (g + 1 < NG) interleave<TM * TN, (AK ? 1 : 2) * TM + (BKM ? 1 : 2) * TN, 0, 0>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt<0>();   // the empty loads past the range have landed too
+    }
+
+    // The tile through LDS and the elementwise epilogue (the LDS ring must be free).
+    __device__ static __forceinline__ void store_staged(const Params& p, char* smem, int m0, int n0, const Acc& acc,
+                                                        int tid, int lane, int wave)
+    {
+        const int wm = wave / WN, wn = wave % WN;
+        store_tile_via_lds<TO, BM, BN, NT, TM * TN * R, SMEM>(
+            p, smem, m0, n0, tid, [&](int v) { return acc[v / (TN * R)][(v / R) % TN][v % R]; },
+            [&](int v, int& r, int& c) {
+                const int i = v / (TN * R), j = (v / R) % TN, q = v % R;
+                c = col(wn, j, lane);
+                r = row(wm, i, q, lane);
+            });
+    }
+
+    // Direct predicated stores of the accumulators, converted to TO.
+    __device__ static __forceinline__ void store_direct(const Params& p, int m0, int n0, const Acc& acc, int lane,
+                                                        int wave)
+    {
+        const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n0 + wn * WTN + j * MI + (lane % MI);
+                const int mb = m0 + wm * WTM + i * MI;
+                if constexpr (MI == 32) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = mb + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
+                        if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = mb + (lane / 16) * 4 + r;
+                        if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
+                    }
+                }
+            }
+        }
+    }
+
+    // The fp32 partial tile, row-major with pitch BN, at p.C, with
+    // device-scope stores (read back by a workgroup that may sit on another
+    // XCD).  row() is linear in q apart from a per-lane part, so each element's
+    // offset is a per-lane VGPR plus a compile-time constant.
+    __device__ static __forceinline__ void store_partial(const Params& p, const Acc& acc, int lane, int wave)
+    {
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, 0x7fffffff, kBufferFlags);
+        const int wm = wave / WN, wn = wave % WN;
+        const int voff = (row(wm, 0, 0, lane) * BN + col(wn, 0, lane)) * 4;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    const int dr = i * MI + (MI == 32 ? (q / 4) * 8 + (q % 4) : q);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[i][j][q]), cr, voff,
+                                                          (dr * BN + j * MI) * 4, kDeviceCoherent);
+                }
+    }
+
+    // The stream-K kernel's interface: COHERENT -> the partial tile at p.C;
+    // else the tile at (m0, n0), through the epilogue when EPI and p.epi.
+    template <bool COHERENT = false, bool EPI = true>
+    __device__ static __forceinline__ void store(const Params& p, int m0, int n0, const Acc& acc, int lane,
+                                                 int wave, char* smem = nullptr)
+    {
+        if constexpr (COHERENT) {
+            store_partial(p, acc, lane, wave);
+        } else {
+            if constexpr (EPI)
+                if (p.epi) {
+                    store_staged(p, smem, m0, n0, acc, wave * 64 + lane, lane, wave);
+                    return;
+                }
+            store_direct(p, m0, n0, acc, lane, wave);
+        }
+    }
+};
+
 // EPI: as for gemm_kernel (a separate instantiation for 16-bit outputs that
 // run the elementwise epilogue).
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_dma_kernel(Params p)
 {
-    static_assert(TI != In::F32, "direct-to-LDS kernel is for 16-bit inputs");
-    constexpr int NW = WM * WN, NT = NW * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / MI, TN = WTN / MI;
-    constexpr int KG = MI == 32 ? 16 : 32;      // k per MFMA
-    constexpr int NG = BK / KG;                 // k-groups per tile
-    using OA = DmaOperand<BM, BK, NW, AK>;
-    using OB = DmaOperand<BN, BK, NW, BKM>;
-    constexpr int STAGE = OA::BYTES + OB::BYTES;
-    constexpr int LPT = OA::IPW + OB::IPW;      // loads per wave per tile
-    static_assert(BK % KG == 0, "BK must be a multiple of the MFMA k");
-    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
-    using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
-
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM>;
+    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
 
     select_batch(p);
     // wave index as a wave-uniform (scalar) value: the LDS addresses of the
     // direct loads (M0) then need no v_readfirstlane per load.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    OA oa;
-    OB ob;
+    typename KT::OA oa;
+    typename KT::OB ob;
     oa.init(wave, lane, p.lda);
     ob.init(wave, lane, p.ldb);
 
-    Acc acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
+    typename KT::Acc acc;
+    KT::zero(acc);
 
+    // The main loop of KT::mainloop for the whole k-range, written out here
+    // (the two must stay in step): through the engine's function, even with
+    // the range fixed at compile time, the compiler gives each fragment its
+    // own LDS base register instead of folding the fragment offsets into the
+    // ds_read offsets -- 12 more instructions per k-tile, 2 % slower.  The
+    // stream-K kernel, which needs arbitrary k-ranges, uses KT::mainloop.
+    constexpr int NG = KT::NG, KG = KT::KG, TM = KT::TM, TN = KT::TN, STAGE = KT::STAGE, LPT = KT::LPT;
+    constexpr int NT = KT::NT, WTM = KT::WTM, WTN = KT::WTN;
+    using OA = typename KT::OA;
+    using OB = typename KT::OB;
+    const int wm = wave / WN, wn = wave % WN;
     const int nkt = (p.K + BK - 1) / BK;
     const int kvalid_last = p.K - (nkt - 1) * BK;
     const bool ragged = kvalid_last != BK;
-
-    // Every k-tile issues the loads of tile t+STAGES-1, also past the last
-    // tile: those get an empty extent (num_records 0) and write zeros into a
-    // stage that no later tile reads.  No branch precedes each k-group's
-    // loads, and the number of loads in flight is the same for every tile.
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) {
         const bool live = s < nkt;
@@ -238,10 +438,7 @@ gemm_dma_kernel(Params p)
         oa.issue(p.A, live ? p.a_bytes : 0, p.lda, m0, s * BK, st, wave);
         ob.issue(p.B, live ? p.b_bytes : 0, p.ldb, n0, s * BK, st + OA::BYTES, wave);
     }
-
     for (int t = 0; t < nkt; ++t) {
-        // Tile t has landed once the STAGES-2 later tiles' loads are all that
-        // remain outstanding.
         wait_vmcnt<LPT * (STAGES - 2)>();
         char* st = smem + (t % STAGES) * STAGE;
         if (t == nkt - 1 && ragged && (AK || BKM)) {
@@ -250,15 +447,11 @@ gemm_dma_kernel(Params p)
             ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
         }
-        // A bare barrier: this wave's loads of tile t are complete (the vmcnt wait
-        // above), so after it every wave's part of tile t is in LDS.  A fenced
-        // __syncthreads() would also wait for the later tiles still in flight.
         bare_barrier();
         const bool more = t + STAGES - 1 < nkt;
         const uint64_t na = more ? p.a_bytes : 0, nb = more ? p.b_bytes : 0;
         char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
         const int nk0 = (t + STAGES - 1) * BK;
-
         const char* sa = st;
         const char* sb = st + OA::BYTES;
         i32x4 fa[2][TM], fb[2][TN];
@@ -272,12 +465,6 @@ gemm_dma_kernel(Params p)
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             __builtin_amdgcn_sched_barrier(0);
-            // This k-group's share of the loads of tile t+STAGES-1 (into the stage
-            // tile t-1 used, which every wave has left at the barrier above),
-            // spread over the first NI k-groups: spread, so the loads do not
-            // leave in one burst after the barrier; within the first half of
-            // the tile, so that with two stages the last share still has half
-            // a tile to land (measured: 2-4 % faster than spreading over all).
             constexpr int NI = NG < 2 ? NG : 2;
             if (g < NI) {
                 oa.issue(p.A, na, p.lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
@@ -297,38 +484,11 @@ gemm_dma_kernel(Params p)
 
     // Epilogue (as in gemm_kernel): fp32 accumulators -> output type, predicated stores.
     if (TO == Out::F32 ? p.epi : EPI) {
-        constexpr int R = MI == 32 ? 16 : 4;
-        store_tile_via_lds<TO, BM, BN, NT, TM * TN * R, STAGES * STAGE>(
-            p, smem, m0, n0, tid, [&](int v) { return acc[v / (TN * R)][(v / R) % TN][v % R]; },
-            [&](int v, int& r, int& c) {
-                const int i = v / (TN * R), j = (v / R) % TN, q = v % R;
-                c = wn * WTN + j * MI + (lane % MI);
-                r = wm * WTM + i * MI + (MI == 32 ? (q / 4) * 8 + (lane / 32) * 4 + (q % 4) : (lane / 16) * 4 + q);
-            });
+        KT::store_staged(p, smem, m0, n0, acc, tid, lane, wave);
         return;
     }
     if constexpr (TO != Out::F32 && EPI) return;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WTN + j * MI + (lane % MI);
-            const int mb = m0 + wm * WTM + i * MI;
-            if constexpr (MI == 32) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = mb + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
-                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = mb + (lane / 16) * 4 + r;
-                    if (m < p.M && n < p.N) store_out<TO>(p.C, (int64_t)m * p.ldc + n, acc[i][j][r]);
-                }
-            }
-        }
-    }
+    KT::store_direct(p, m0, n0, acc, lane, wave);
 }
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES>

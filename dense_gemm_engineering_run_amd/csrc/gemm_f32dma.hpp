@@ -29,6 +29,7 @@
 #pragma once
 
 #include "gemm_dma.hpp"
+#include "gemm_streamk.hpp"
 
 namespace mg {
 
@@ -148,6 +149,8 @@ struct Units {
 // and the epilogue that stores a C tile.
 template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
 struct F32Dma {
+    static constexpr int TILE_M = BM, TILE_N = BN, TILE_K = BK;
+    static constexpr Out OUT = TO;
     static constexpr int NW = WM * WN, NT = NW * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     using UA = Units<AK, WTM>;
@@ -405,150 +408,6 @@ gemm_f32dma_kernel(Params p)
     KT::store(p, m0, n0, acc, lane, wave, smem);
 }
 
-// Persistent stream-K form of the same kernel, for grids that would leave
-// part of the chip idle in their last wave (the persistent, load-balanced
-// tile scheduling of the Gluon multi-CTA tutorial, "Persistent kernels" and
-// its cluster launch control scheduler, reshaped for CDNA's plain grid).
-//
-// p.grid workgroups run (a multiple of 8; workgroup w runs on XCD w mod 8).
-//  * Tiles [0, sk_first) are data-parallel: logical id g (XCD-major rank of
-//    w) takes tiles g, g + grid, ...
-//  * The k-iterations of the remaining tiles, tile after tile, are split into
-//    sk_wgs contiguous ranges (sk_base or sk_base + 1 iterations each), one
-//    per stream-K id; consecutive ids share an XCD and every XCD gets
-//    sk_wgs / 8 of them.  A workgroup whose range covers a whole tile stores
-//    it directly.  A tile split over several workgroups is finished by the
-//    last one to arrive: every contributor writes its partial tile (fp32,
-//    row-major) to its workspace slot, waits until the writes are
-//    acknowledged, then increments the tile's counter atomically; the one
-//    that sees the count reach the contributor count adds the partial tiles
-//    in contributor order, stores C and resets the counter to zero.  Nobody
-//    waits for anybody, and the order of the sum depends only on the
-//    schedule, so results are deterministic.
-//
-// Coherence: the XCDs' L2 caches are not coherent with each other.  Partial
-// tiles are written and read with device-scope cache policy (sc1, the
-// encoding the compiler gives agent-scope atomic loads and stores), and the
-// counter is an agent-scope atomic issued only after every partial write of
-// the workgroup has completed (s_waitcnt vmcnt(0), then the barrier), so no
-// whole-L2 write-back or invalidate is needed.
-template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_f32dma_sk_kernel(Params p)
-{
-    using KT = F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>;
-    static_assert(TO == Out::F32, "stream-K partial tiles are fp32");
-    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
-    __shared__ int arrived;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = p.grid;
-    const int xcd = blockIdx.x % 8, rank = blockIdx.x / 8;
-    const int g = xcd * (G / 8) + rank;
-    const int nkt = (p.K + BK - 1) / BK;
-
-    typename KT::OA oa;
-    typename KT::OB ob;
-    oa.init(wave, lane, p.lda);
-    ob.init(wave, lane, p.ldb);
-    typename KT::Acc acc;
-
-    // Stream-K id: sk_wgs is a multiple of 8 (or below 8: XCDs 0 .. sk_wgs-1).
-    const int per_xcd = p.sk_wgs >= 8 ? p.sk_wgs / 8 : 1;
-    const bool streams = rank < per_xcd && xcd * per_xcd + rank < p.sk_wgs;
-    const int k = xcd * per_xcd + rank;
-
-    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(p.sk_part, (short)0, 0x7fffffff, kBufferFlags);
-    const int base = p.sk_base, rem = p.sk_rem;
-    auto start = [&](int w) { return w * base + min(w, rem); };
-    auto owner = [&](int i) {
-        const int cut = rem * (base + 1);
-        return i < cut ? i / (base + 1) : rem + (i - cut) / base;
-    };
-    // Work units: this workgroup's data-parallel tiles, then its stream-K range.
-    int L = g;
-    int it = streams ? start(k) : 0;
-    const int end = streams ? start(k + 1) : 0;
-    while (true) {
-        int tile, kt0, kt1, s = -1;
-        if (L < p.sk_first) {
-            tile = L;
-            kt0 = 0;
-            kt1 = nkt;
-            L += G;
-        } else if (it < end) {
-            s = it / nkt;
-            kt0 = it - s * nkt;
-            kt1 = min(nkt, kt0 + (end - it));
-            tile = p.sk_first + s;
-            it += kt1 - kt0;
-        } else {
-            break;
-        }
-        int tm, tn;
-        raster(p, tile, tm, tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        KT::zero(acc);
-        KT::mainloop(p, smem, oa, ob, m0, n0, kt0, kt1, acc, tid, lane, wave);
-        if (kt0 == 0 && kt1 == nkt) {
-            if constexpr (sk_epilogue_ok(BM, BN)) KT::template store<false, true>(p, m0, n0, acc, lane, wave, smem);
-            else KT::template store<false, false>(p, m0, n0, acc, lane, wave);
-        } else {
-            const int ts = s * nkt;
-            const int gf = owner(ts), gl = owner(ts + nkt - 1);
-            // Slot of contributor w for this tile: 2w when the tile is w's first
-            // range piece, 2w + 1 when it is its last (w started in an earlier tile).
-            auto slot = [&](int w) { return (2 * w + (start(w) >= ts ? 0 : 1)) * KT::PART_BYTES; };
-            {
-                Params q = p;                 // the partial tile, row-major BM x BN
-                q.C = (char*)p.sk_part + slot(k);
-                q.ldc = BN;
-                KT::template store<true>(q, 0, 0, acc, lane, wave);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (tid == 0)
-                arrived = __hip_atomic_fetch_add(p.sk_count + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            if (arrived == gl - gf) {
-                // Last to arrive: C = partial(gf) + ... + partial(gl).  Thread
-                // tid owns the 16-byte chunks tid + NT*u of the row-major
-                // tile; U chunks per batch keep U loads in flight (fewer for
-                // small tiles, whose kernels run two workgroups per CU and
-                // must stay within 256 registers).
-                constexpr int CH = BM * BN / 4 / KT::NT, UMAX = BM * BN > 128 * 128 ? 16 : 8;
-                constexpr int U = CH < UMAX ? CH : UMAX;
-                static_assert(CH % U == 0, "reduction batches");
-                auto part = [&](int w, int c) {
-                    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         wsr, slot(w) + tid * 16, c * KT::NT * 16, kDeviceCoherent));
-                };
-#pragma unroll 1
-                for (int b = 0; b < CH; b += U) {
-                    f32x4 sum[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) sum[u] = part(gf, b + u);
-                    for (int w = gf + 1; w <= gl; ++w) {
-                        f32x4 t[U];
-#pragma unroll
-                        for (int u = 0; u < U; ++u) t[u] = part(w, b + u);
-#pragma unroll
-                        for (int u = 0; u < U; ++u) sum[u] += t[u];
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int idx = tid + (b + u) * KT::NT;
-                        const int m = m0 + idx / (BN / 4), n = n0 + (idx % (BN / 4)) * 4;
-                        if (m < p.M) store4<TO>(p, m, n, sum[u]);   // the elementwise epilogue, if any
-                    }
-                }
-                if (tid == 0) __hip_atomic_store(p.sk_count + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        bare_barrier();                       // the LDS ring (and `arrived`) are reused next
-    }
-}
-
 template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SK = false>
 struct F32DmaInst {
     template <bool AK, bool BKM>
@@ -557,7 +416,7 @@ struct F32DmaInst {
         Params copy = p;
         void* args[] = {&copy};
         if constexpr (SK)
-            return hipLaunchKernel((const void*)&gemm_f32dma_sk_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
+            return hipLaunchKernel((const void*)&gemm_sk_kernel<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>>,
                                    dim3((unsigned)p.grid), dim3(WM * WN * 64), args, 0, s);
         return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
