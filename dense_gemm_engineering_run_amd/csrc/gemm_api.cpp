@@ -278,11 +278,13 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
 }
 
 // Built-in choice among the element-by-element configs (operands that are
-// not 16-byte aligned).
+// not 16-byte aligned): fp32 problems of at least 64 tiles of 128x128 take
+// the 4-byte direct-to-LDS loads, the rest the register-staged element loads.
 int heuristic_scalar(int dtype, int64_t M, int64_t N)
 {
-    const std::string tile = std::ceil(M / 128.0) * std::ceil(N / 128.0) >= 64
-                                 ? (dtype == GEMM_DTYPE_F32 ? "128x128x16 w2x2 mfma32" : "128x128x64 w2x2 mfma32")
+    const bool big = std::ceil(M / 128.0) * std::ceil(N / 128.0) >= 64;
+    if (dtype == GEMM_DTYPE_F32 && big) return find_config(dtype, "f32 128x128x32 w2x2 mfma32 s2 dma scalar");
+    const std::string tile = big ? (dtype == GEMM_DTYPE_F32 ? "128x128x16 w2x2 mfma32" : "128x128x64 w2x2 mfma32")
                                  : (dtype == GEMM_DTYPE_F32 ? "64x64x16 w2x2 mfma16" : "64x64x64 w2x2 mfma16");
     return find_config(dtype, std::string(kDtypes[dtype].name) + " " + tile + " s2 swz scalar");
 }

@@ -17,12 +17,18 @@ namespace mg {
     {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma sk",            \
      BM, BN, BK, WM, WN, 32, true, &F32DmaInst<Out::F32, BM, BN, BK, WM, WN, ST, true>::launch, ST, true, OCC},
 
+#define MG_F32DMA_SCALAR_ENTRY(BM, BN, BK, WM, WN, ST)                               \
+    {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma scalar",        \
+     BM, BN, BK, WM, WN, 32, true,                                                  \
+     &F32DmaInst<Out::F32, BM, BN, BK, WM, WN, ST, false, false>::launch, ST, true, 0, true},
+
 #define MG_SCALAR_ENTRY(BM, BN, BK, WM, WN, MI)                                        \
     {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2 swz scalar",              \
      BM, BN, BK, WM, WN, MI, true, &Inst<In::F32, Out::F32, BM, BN, BK, WM, WN, MI, true, false>::launch, 2, false, 0, true},
 
 static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIGS(MG_F32DMA_ENTRY)
                                            MG_F32DMA_SK_CONFIGS(MG_F32DMA_SK_ENTRY)
+                                           MG_F32DMA_SCALAR_CONFIGS(MG_F32DMA_SCALAR_ENTRY)
                                            MG_SCALAR_CONFIGS_F32(MG_SCALAR_ENTRY)};
 
 const KernelEntry* entries_f32(int* n)

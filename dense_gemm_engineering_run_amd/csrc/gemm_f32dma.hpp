@@ -33,31 +33,40 @@
 
 namespace mg {
 
-// One fp32 operand's k-tile in the LDS ring.
-template <int ROWS, int BK, int NWAVES, bool KMAJ>
+// One fp32 operand's k-tile in the LDS ring.  VEC: each 1 KB group of the
+// tile is one load of 16 bytes per lane (the operand and its leading
+// dimension 16-byte aligned); else four loads of 4 bytes per lane, lane l of
+// load e filling element l % 4 of 16-byte slot 16e + l / 4 -- the same LDS
+// layout, for operands aligned only to their elements.
+template <int ROWS, int BK, int NWAVES, bool KMAJ, bool VEC = true>
 struct F32Operand {
     static constexpr int ES = 4, CE = 4;
     static constexpr int BYTES = ROWS * BK * ES;
-    static constexpr int IPW = BYTES / 1024 / NWAVES;
+    static constexpr int IPW = BYTES / 1024 / NWAVES;       // 1 KB groups per wave per tile
     static_assert(BYTES % (1024 * NWAVES) == 0, "tile must split into 1 KB loads per wave");
+    static constexpr int SUB = VEC ? 1 : 4;                 // loads per group
+    static constexpr int LOADS = IPW * SUB;                 // load instructions per wave per tile
     static constexpr int CPR = BK / CE, RB = BK * ES;       // k-contiguous layout
     static constexpr int RCH = ROWS / CE, RBM = ROWS * ES;  // m-contiguous layout (no swizzle:
                                                             // its reads are contiguous)
-    int voff[IPW];
+    int voff[LOADS];
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
     {
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-            const int slot = (wave * IPW + j) * 64 + lane;
-            if (KMAJ) {
-                const int row = slot / CPR, phys = slot % CPR;
-                voff[j] = (int)(row * ld * ES) + swz_chunk<CPR, true>(row, phys) * 16;
-            } else {
-                const int k = slot / RCH, c = slot % RCH;
-                voff[j] = (int)(k * ld * ES) + c * 16;
+        for (int j = 0; j < IPW; ++j)
+#pragma unroll
+            for (int e = 0; e < SUB; ++e) {
+                const int slot = (wave * IPW + j) * 64 + (VEC ? lane : 16 * e + lane / 4);
+                const int elem = VEC ? 0 : (lane % 4) * ES;
+                if (KMAJ) {
+                    const int row = slot / CPR, phys = slot % CPR;
+                    voff[j * SUB + e] = (int)(row * ld * ES) + swz_chunk<CPR, true>(row, phys) * 16 + elem;
+                } else {
+                    const int k = slot / RCH, c = slot % RCH;
+                    voff[j * SUB + e] = (int)(k * ld * ES) + c * 16 + elem;
+                }
             }
-        }
     }
 
     __device__ __forceinline__ void issue(const char* base, uint64_t bytes, int64_t ld, int row0,
@@ -75,10 +84,20 @@ struct F32Operand {
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
             if (j < j0 || j >= j1) continue;
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :
-                         : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024)), "v"(voff[j]), "s"(rs)
-                         : "memory", "m0");
+            if constexpr (VEC) {
+                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                             :
+                             : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024)), "v"(voff[j]), "s"(rs)
+                             : "memory", "m0");
+            } else {
+#pragma unroll
+                for (int e = 0; e < SUB; ++e)
+                    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                                 :
+                                 : "s"(__builtin_amdgcn_readfirstlane(lds0 + j * 1024 + e * 256)),
+                                   "v"(voff[j * SUB + e]), "s"(rs)
+                                 : "memory", "m0");
+            }
         }
     }
 
@@ -147,7 +166,7 @@ struct Units {
 
 // The pieces of the kernel: a main loop over a range of k-tiles of one C tile,
 // and the epilogue that stores a C tile.
-template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM, bool VEC = true>
 struct F32Dma {
     static constexpr int TILE_M = BM, TILE_N = BN, TILE_K = BK;
     static constexpr Out OUT = TO;
@@ -157,10 +176,10 @@ struct F32Dma {
     using UB = Units<BKM, WTN>;
     static constexpr int NA = UA::N, NB = UB::N;
     static constexpr int NG = BK / 8;                  // 8-k steps per tile
-    using OA = F32Operand<BM, BK, NW, AK>;
-    using OB = F32Operand<BN, BK, NW, BKM>;
+    using OA = F32Operand<BM, BK, NW, AK, VEC>;
+    using OB = F32Operand<BN, BK, NW, BKM, VEC>;
     static constexpr int STAGE = OA::BYTES + OB::BYTES;
-    static constexpr int LPT = OA::IPW + OB::IPW;
+    static constexpr int LPT = OA::LOADS + OB::LOADS;   // load instructions per wave per tile
     static constexpr int SMEM = STAGES * STAGE;
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
     static_assert(STAGES >= 2 && SMEM <= 160 * 1024, "LDS budget");
@@ -382,11 +401,11 @@ struct F32Dma {
     static constexpr int PART_BYTES = BM * BN * 4;   // one partial tile, fp32 row-major
 };
 
-template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM>
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool AK, bool BKM, bool VEC>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_f32dma_kernel(Params p)
 {
-    using KT = F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>;
+    using KT = F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM, VEC>;
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
 
     select_batch(p);
@@ -408,7 +427,9 @@ gemm_f32dma_kernel(Params p)
     KT::store(p, m0, n0, acc, lane, wave, smem);
 }
 
-template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SK = false>
+// SK: the persistent stream-K kernel.  VEC = false: element-aligned operands
+// (4-byte direct loads).
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SK = false, bool VEC = true>
 struct F32DmaInst {
     template <bool AK, bool BKM>
     static hipError_t go(const Params& p, hipStream_t s)
@@ -418,7 +439,7 @@ struct F32DmaInst {
         if constexpr (SK)
             return hipLaunchKernel((const void*)&gemm_sk_kernel<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>>,
                                    dim3((unsigned)p.grid), dim3(WM * WN * 64), args, 0, s);
-        return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM>,
+        return hipLaunchKernel((const void*)&gemm_f32dma_kernel<TO, BM, BN, BK, WM, WN, STAGES, AK, BKM, VEC>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)

@@ -75,7 +75,7 @@ def test_unaligned_operands_take_the_scalar_configs_without_gpu():
     fails only for lack of a GPU here) and run on the element-by-element
     configs; a forced 16-byte config is refused."""
     scalar = [i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i).endswith("scalar")]
-    assert len(scalar) == 2
+    assert len(scalar) == 4          # fp32: two with 4-byte direct loads, two register-staged
     for kw in (dict(K=30, lda=30, ldb=32), dict(A=P + 4), dict(C=3 * P + 8), dict(ldc=65),
                dict(K=60, dtype=1, lda=60, ldb=64), dict(A=P + 2, dtype=2)):
         assert run(**kw) == b.GEMM_ERR_HIP, kw
@@ -88,7 +88,9 @@ def test_unaligned_operands_take_the_scalar_configs_without_gpu():
                              scalar[1]) == b.GEMM_ERR_HIP
     for d in range(5):
         assert sum(g.gemm_config_describe(d, i).endswith("scalar")
-                   for i in range(g.gemm_num_configs(d))) == 2
+                   for i in range(g.gemm_num_configs(d))) == (4 if d == 0 else 2)
+    # the large unaligned fp32 problems take the direct-to-LDS element loads
+    assert g.gemm_config_describe(0, g.gemm_select_config(4095, 2049, 1028, "k", "k", "n", 0)) != ""
 
 
 def test_degenerate_sizes_without_gpu():
