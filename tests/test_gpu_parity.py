@@ -684,6 +684,9 @@ def test_unaligned_operands_every_layout(dtype):
         assert used.endswith("scalar"), used
         for cfg in scalar:
             unaligned_case(97, 65, 37, layout, dtype, "int5", pads=(3, 1, 5), offs=(3, 1, 2), config=cfg)
+            # several tiles and k-tiles, a partial last k-tile
+            unaligned_case(300, 260, 100, layout, dtype, "int5", pads=(1, 5, 3), offs=(1, 3, 3), config=cfg,
+                           seed=23)
     log(f"{dtype}: unaligned operands, 8 layouts")
 
 
