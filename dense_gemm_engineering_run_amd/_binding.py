@@ -15,7 +15,7 @@ DEFAULT_TABLE = os.path.join(HERE, "tuning", "table.txt")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m dense_gemm_engineering_run_amd.build, or __graft_entry__.build())")
+        "(python dense_gemm_engineering_run_amd/build.py, or __graft_entry__.build())")
 
 # PyTorch (used for device memory and streams) ships its own HIP runtime with
 # the same SONAME as /opt/rocm's.  Loading torch first makes the library bind
