@@ -377,14 +377,6 @@ uint64_t workspace_need(const mg::KernelEntry& e, int64_t M, int64_t N, int64_t 
     return sk_plan(e, tiles, (K + e.BK - 1) / e.BK).bytes;
 }
 
-// A stream-K config that cannot run an active epilogue (sk_epilogue_ok).
-bool sk_without_epilogue(int dtype, int config)
-{
-    int n = 0;
-    const mg::KernelEntry* all = entries(dtype, &n);
-    return config >= 0 && config < n && all[config].sk_occ > 0 && !mg::sk_epilogue_ok(all[config].BM, all[config].BN);
-}
-
 // True when the epilogue does something (else the plain store runs).
 bool epi_active(const gemm_epilogue_t* epi)
 {
@@ -392,10 +384,10 @@ bool epi_active(const gemm_epilogue_t* epi)
 }
 
 // The config gemm_run* launches when none is forced: the table's choice,
-// unless it is a stream-K config that cannot run here (batched call, an
-// epilogue, or no workspace of the size it needs), then the heuristic.
+// unless it is a stream-K config that cannot run here (batched call, or no
+// workspace of the size it needs), then the heuristic.
 int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
-                        uint64_t ws_bytes, bool epi, bool vec16)
+                        uint64_t ws_bytes, bool vec16)
 {
     if (!vec16) return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
     int n = 0;
@@ -403,8 +395,7 @@ int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N,
     const bool swap = c == 'm';
     auto usable = [&](int config) {
         const mg::KernelEntry& e = all[config];
-        return e.sk_occ == 0 || (batch == 1 && (!epi || mg::sk_epilogue_ok(e.BM, e.BN)) &&
-                                 workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
+        return e.sk_occ == 0 || (batch == 1 && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
     };
     return select(dtype, a, b, c, M, N, K, batch, usable);
 }
@@ -418,21 +409,21 @@ struct SelectMemo {
     char a = 0, b = 0, c = 0;
     int64_t M = 0, N = 0, K = 0, batch = 0;
     uint64_t ws_bytes = 0;
-    bool epi = false, vec16 = false;
+    bool vec16 = false;
     int config = -1;
 };
 thread_local SelectMemo t_memo;
 
 int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
-               uint64_t ws_bytes, bool epi = false, bool vec16 = true)
+               uint64_t ws_bytes, bool vec16 = true)
 {
     const unsigned gen = g_table_gen.load();
     SelectMemo& m = t_memo;
     if (m.valid && m.gen == gen && m.dtype == dtype && m.a == a && m.b == b && m.c == c && m.M == M &&
-        m.N == N && m.K == K && m.batch == batch && m.ws_bytes == ws_bytes && m.epi == epi && m.vec16 == vec16)
+        m.N == N && m.K == K && m.batch == batch && m.ws_bytes == ws_bytes && m.vec16 == vec16)
         return m.config;
-    const int config = select_for_uncached(dtype, a, b, c, M, N, K, batch, ws_bytes, epi, vec16);
-    m = SelectMemo{true, gen, dtype, a, b, c, M, N, K, batch, ws_bytes, epi, vec16, config};
+    const int config = select_for_uncached(dtype, a, b, c, M, N, K, batch, ws_bytes, vec16);
+    m = SelectMemo{true, gen, dtype, a, b, c, M, N, K, batch, ws_bytes, vec16, config};
     return config;
 }
 
@@ -517,14 +508,13 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
         if (!vec16 && !is_scalar(dtype, config)) return GEMM_ERR_MISALIGNED;   // needs 16-byte loads
     }
     if (epi && (epi->activation < GEMM_ACT_NONE || epi->activation > GEMM_ACT_GELU)) return GEMM_ERR_BAD_EPILOGUE;
-    if (epi_active(epi) && sk_without_epilogue(dtype, config)) return GEMM_ERR_BAD_EPILOGUE;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     Canon x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc, vec16);
     x.batch = batch;
     x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
     x.sb = c == 'm' ? sa : sb;
     x.sc = sc;
-    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, epi_active(epi), vec16);
+    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, vec16);
     if (config < 0) return GEMM_ERR_NO_CONFIG;
     // bias follows the user's columns n: the canonical rows when C is m-major.
     return launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
@@ -614,7 +604,7 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_HIP: return "HIP runtime error at launch";
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
     case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
-    case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation, or an epilogue on a config without one";
+    case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation";
     default: return "unknown status";
     }
 }

@@ -310,12 +310,14 @@ struct Dma16 {
         wait_vmcnt<0>();   // the empty loads past the range have landed too
     }
 
-    // The tile through LDS and the elementwise epilogue (the LDS ring must be free).
+    // The tile through LDS and the elementwise epilogue (the LDS ring must be
+    // free); ROLLED as for store_tile_via_lds.
+    template <bool ROLLED = false>
     __device__ static __forceinline__ void store_staged(const Params& p, char* smem, int m0, int n0, const Acc& acc,
                                                         int tid, int lane, int wave)
     {
         const int wm = wave / WN, wn = wave % WN;
-        store_tile_via_lds<TO, BM, BN, NT, TM * TN * R, SMEM>(
+        store_tile_via_lds<TO, BM, BN, NT, TM * TN * R, SMEM, ROLLED>(
             p, smem, m0, n0, tid, [&](int v) { return acc[v / (TN * R)][(v / R) % TN][v % R]; },
             [&](int v, int& r, int& c) {
                 const int i = v / (TN * R), j = (v / R) % TN, q = v % R;
@@ -374,8 +376,9 @@ struct Dma16 {
     }
 
     // The stream-K kernel's interface: COHERENT -> the partial tile at p.C;
-    // else the tile at (m0, n0), through the epilogue when EPI and p.epi.
-    template <bool COHERENT = false, bool EPI = true>
+    // else the tile at (m0, n0), through the epilogue when EPI and p.epi
+    // (ROLLED as for store_tile_via_lds).
+    template <bool COHERENT = false, bool EPI = true, bool ROLLED = false>
     __device__ static __forceinline__ void store(const Params& p, int m0, int n0, const Acc& acc, int lane,
                                                  int wave, char* smem = nullptr)
     {
@@ -384,7 +387,7 @@ struct Dma16 {
         } else {
             if constexpr (EPI)
                 if (p.epi) {
-                    store_staged(p, smem, m0, n0, acc, wave * 64 + lane, lane, wave);
+                    store_staged<ROLLED>(p, smem, m0, n0, acc, wave * 64 + lane, lane, wave);
                     return;
                 }
             store_direct(p, m0, n0, acc, lane, wave);

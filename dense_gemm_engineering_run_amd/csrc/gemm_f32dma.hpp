@@ -317,8 +317,9 @@ struct F32Dma {
     // COHERENT: write with device-scope cache policy (partial tiles of the
     // stream-K kernel, read by a workgroup that may sit on another XCD).
     // With EPI and p.epi set the tile goes through the elementwise epilogue
-    // via LDS, which must be free (smem = the kernel's LDS ring).
-    template <bool COHERENT = false, bool EPI = true>
+    // via LDS, which must be free (smem = the kernel's LDS ring); ROLLED as
+    // for store_tile_via_lds.
+    template <bool COHERENT = false, bool EPI = true, bool ROLLED = false>
     __device__ static __forceinline__ void store(const Params& p, int m0, int n0, const Acc& acc, int lane,
                                                  int wave, char* smem = nullptr)
     {
@@ -326,7 +327,7 @@ struct F32Dma {
         const int wm = wave / WN, wn = wave % WN;
         const int rm0 = m0 + wm * WTM, cn0 = n0 + wn * WTN;
         if (!COHERENT && EPI && p.epi) {
-            store_tile_via_lds<TO, BM, BN, NT, NA * NB * 16, SMEM>(
+            store_tile_via_lds<TO, BM, BN, NT, NA * NB * 16, SMEM, ROLLED>(
                 p, smem, m0, n0, wave * 64 + lane, [&](int v) { return acc[v / (NB * 16)][(v / 16) % NB][v % 16]; },
                 [&](int v, int& r, int& c) {
                     const int i = v / (NB * 16), j = (v / 16) % NB, q = v % 16;

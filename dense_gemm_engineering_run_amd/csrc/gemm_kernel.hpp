@@ -475,8 +475,10 @@ __device__ __forceinline__ void store4(const Params& p, int m, int n, f32x4 v)
 // of the epilogue code.  get(v) returns accumulator v (a constant index once
 // the loops are unrolled), pos(v, r, c) its tile-local row and column.  The
 // LDS (LDS_BYTES from smem) must be free: a barrier follows the main loop
-// here before anything is written.
-template <Out TO, int BM, int BN, int NT, int NV, int LDS_BYTES, class Get, class Pos>
+// here before anything is written.  ROLLED keeps the loop over bands rolled
+// (fewer registers live at once: the persistent stream-K kernels, whose loop
+// state stays live across the store, need that for 256x256 tiles).
+template <Out TO, int BM, int BN, int NT, int NV, int LDS_BYTES, bool ROLLED = false, class Get, class Pos>
 __device__ __forceinline__ void store_tile_via_lds(const Params& p, char* smem, int m0, int n0, int tid,
                                                    Get get, Pos pos)
 {
@@ -484,9 +486,7 @@ __device__ __forceinline__ void store_tile_via_lds(const Params& p, char* smem, 
     constexpr int RB = FIT >= BM ? BM : FIT >= 128 ? 128 : FIT >= 64 ? 64 : FIT >= 32 ? 32 : FIT >= 16 ? 16 : 8;
     static_assert(FIT >= 8 && BM % RB == 0, "LDS too small for the staged epilogue");
     float* t = (float*)smem;
-    __syncthreads();
-#pragma unroll
-    for (int b0 = 0; b0 < BM; b0 += RB) {
+    auto band = [&](int b0) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             int r, c;
@@ -501,6 +501,14 @@ __device__ __forceinline__ void store_tile_via_lds(const Params& p, char* smem, 
             if (m < p.M) store4<TO>(p, m, n0 + c, *(const f32x4*)(t + r * BN + c));
         }
         __syncthreads();
+    };
+    __syncthreads();
+    if constexpr (ROLLED) {
+#pragma unroll 1
+        for (int b0 = 0; b0 < BM; b0 += RB) band(b0);
+    } else {
+#pragma unroll
+        for (int b0 = 0; b0 < BM; b0 += RB) band(b0);
     }
 }
 
@@ -773,13 +781,6 @@ gemm_kernel(Params p)
 
 // One tile configuration, instantiated for the four operand layouts.
 using LaunchFn = hipError_t (*)(int layout, const Params& p, hipStream_t s);
-
-// Whether a stream-K config runs the elementwise epilogue on the tiles it
-// completes in one range (staged through LDS as in the other kernels): the
-// 256x256 stream-K kernels have no registers left for it (their accumulators
-// take 256 per lane), so only smaller tiles do.  Tiles finished by the
-// reduction of partials always could; the rule is per config.
-constexpr bool sk_epilogue_ok(int BM, int BN) { return BM * BN <= 128 * 128; }
 
 struct KernelEntry {
     const char* name;

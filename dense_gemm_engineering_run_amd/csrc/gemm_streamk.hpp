@@ -42,6 +42,9 @@ gemm_sk_kernel(Params p)
 {
     constexpr int BM = KT::TILE_M, BN = KT::TILE_N, BK = KT::TILE_K;
     constexpr Out TO = KT::OUT;
+    // Tiles above 128 x 128 hold 256 accumulators per lane: their staged
+    // epilogue keeps its loop over row bands rolled.
+    constexpr bool kBigTile = BM * BN > 128 * 128;
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
     __shared__ int arrived;
 
@@ -95,8 +98,7 @@ gemm_sk_kernel(Params p)
         KT::zero(acc);
         KT::mainloop(p, smem, oa, ob, m0, n0, kt0, kt1, acc, tid, lane, wave);
         if (kt0 == 0 && kt1 == nkt) {
-            if constexpr (sk_epilogue_ok(BM, BN)) KT::template store<false, true>(p, m0, n0, acc, lane, wave, smem);
-            else KT::template store<false, false>(p, m0, n0, acc, lane, wave);
+            KT::template store<false, true, kBigTile>(p, m0, n0, acc, lane, wave, smem);
         } else {
             const int ts = s * nkt;
             const int gf = owner(ts), gl = owner(ts + nkt - 1);
@@ -117,11 +119,11 @@ gemm_sk_kernel(Params p)
             if (arrived == gl - gf) {
                 // Last to arrive: C = partial(gf) + ... + partial(gl).  Thread
                 // tid owns the 16-byte chunks tid + NT*u of the row-major
-                // tile; U chunks per batch keep U loads in flight (fewer for
-                // small tiles, whose kernels run two workgroups per CU and
-                // must stay within 256 registers).
-                constexpr int CH = BM * BN / 4 / KT::NT, UMAX = BM * BN > 128 * 128 ? 16 : 8;
-                constexpr int U = CH < UMAX ? CH : UMAX;
+                // tile; U chunks per batch keep U loads in flight.  Eight, not
+                // more: the 128x128 kernels run two workgroups per CU within
+                // 256 registers, and the 256x256 ones keep their loop state
+                // and the epilogue's loads of old values and bias live here.
+                constexpr int CH = BM * BN / 4 / KT::NT, U = CH < 8 ? CH : 8;
                 static_assert(CH % U == 0, "reduction batches");
                 auto part = [&](int w, int c) {
                     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(

@@ -84,7 +84,7 @@ typedef enum {
     GEMM_ERR_NO_CONFIG = 8,    /* config id out of range for this dtype                  */
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
     GEMM_ERR_TUNING_FILE = 10, /* tuning table missing or malformed                      */
-    GEMM_ERR_BAD_EPILOGUE = 11, /* unknown activation, or an epilogue on a 256x256 stream-K config */
+    GEMM_ERR_BAD_EPILOGUE = 11, /* unknown epilogue activation                              */
     GEMM_ERR_WORKSPACE = 12    /* stream-K config without a large enough workspace       */
 } gemm_status_t;
 
@@ -175,11 +175,8 @@ int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, cha
  * gemm_run_ws with an elementwise epilogue (NULL: none).  Errors besides
  * gemm_run_ws's: bias not 4-byte aligned -> GEMM_ERR_MISALIGNED; bias
  * overlapping C -> GEMM_ERR_ALIAS; unknown activation -> GEMM_ERR_BAD_EPILOGUE.
- * The stream-K configs with tiles of at most 128x128 run the epilogue (once
- * per element, by the workgroup that completes the tile); an epilogue that is
- * not the identity with a forced 256x256 stream-K config ->
- * GEMM_ERR_BAD_EPILOGUE (their registers are full), and config_id < 0 then
- * chooses among the others.
+ * Every config runs the epilogue; in a stream-K config it is applied once per
+ * element, by the workgroup that completes the tile.
  */
 int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                 int dtype, const void* A, const void* B, void* C,

@@ -191,8 +191,8 @@ def test_epilogue_errors_without_gpu():
     assert run_ex(g.Epilogue(1.0, 0.0, 3 * P + 64, 0)) == b.GEMM_ERR_ALIAS   # bias inside C
     assert run_ex(g.Epilogue(1.0, 0.0, 0, 7)) == b.GEMM_ERR_BAD_EPILOGUE
     assert run_ex(g.Epilogue(1.0, 0.0, 0, -1)) == b.GEMM_ERR_BAD_EPILOGUE
-    # A forced 256x256 stream-K config refuses an active epilogue; a 128x128
-    # one accepts it (and then needs its workspace).
+    # Forced stream-K configs of either tile size accept an active epilogue
+    # (and then need their workspace).
     def sk_id(name):
         return next(i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i) == name)
     relu = g.Epilogue(1.0, 0.0, 0, g.GEMM_ACT_RELU)
@@ -200,7 +200,7 @@ def test_epilogue_errors_without_gpu():
     def run_sk(config, epi):
         return g.gemm_run_ex(4095, 2049, 1028, "k", "k", "n", 0, P, P + (1 << 24), 1 << 32, 1028, 1028,
                              2052, epi, 0, 0, 0, config)
-    assert run_sk(big, relu) == b.GEMM_ERR_BAD_EPILOGUE
+    assert run_sk(big, relu) == b.GEMM_ERR_WORKSPACE
     assert run_sk(big, g.Epilogue(1.0, 0.0, 0, g.GEMM_ACT_NONE)) == b.GEMM_ERR_WORKSPACE   # identity
     assert run_sk(small, relu) == b.GEMM_ERR_WORKSPACE
     # argument errors come first, in status order

@@ -579,12 +579,9 @@ def test_epilogue_every_config_exact(dtype):
     code = gi.DTYPE_CODE[dtype]
     for cfg in range(g.gemm_num_configs(code)):
         name = g.gemm_config_describe(code, cfg)
-        # 256x256 stream-K kernels have no registers for the epilogue
-        expect = g.GEMM_ERR_BAD_EPILOGUE if name.endswith(" sk") and " 256x256x" in name else 0
         for layout in [("k", "k", "n"), ("m", "n", "m")]:
-            epi_case(300, 200, 136, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg,
-                     expect=expect)
-        log(f"{name}: epilogue exact" if not expect else f"{name}: epilogue refused")
+            epi_case(300, 200, 136, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg)
+        log(f"{name}: epilogue exact")
 
 
 def test_epilogue_stream_k_ragged():
@@ -600,6 +597,26 @@ def test_epilogue_stream_k_ragged():
                         config=config, seed=21)
         assert used == sk, g.gemm_config_describe(0, used)
     log("ragged 4095x2049x1028 with epilogue on stream-K: exact")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16_bf16", "f16_f32"])
+def test_epilogue_stream_k_256_whole_and_split_tiles(dtype):
+    """The 256x256 stream-K configs with an epilogue: 17 x 16 = 272 tiles on
+    a grid of 256 workgroups, so 256 whole tiles go through the staged
+    epilogue and 16 split tiles (three contributors each) through the
+    reduction's; bit-exact on integer inputs, C n-major and m-major."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    names = [n for n in (g.gemm_config_describe(code, i) for i in range(g.gemm_num_configs(code)))
+             if n.endswith(" sk") and " 256x256x" in n]
+    assert names
+    for name in names:
+        cfg = next(i for i in range(g.gemm_num_configs(code)) if g.gemm_config_describe(code, i) == name)
+        k = 72 if dtype == "f32" else 136          # three k-tiles, the last one partial
+        for layout, (M, N) in [(("k", "k", "n"), (4352, 4096)), (("m", "n", "m"), (4096, 4352))]:
+            used = epi_case(M, N, k, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg, seed=23)
+            assert used == cfg
+        log(f"{name}: 256 whole + 16 split tiles with epilogue exact")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
