@@ -314,7 +314,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the engine runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the GEMM would shard along M or N with a broadcast of B, which is not built).",
               file=sys.stderr)
         sys.exit(2)

@@ -226,7 +226,7 @@ int parse_table(const char* path, std::vector<TuneEntry>& out)
         if (d < 0 || a.size() != 1 || b.size() != 1 || c.size() != 1 || M < 0 || N < 0 || K < 0)
             return GEMM_ERR_TUNING_FILE;
         int id = find_config(d, cfg);
-        if (id < 0) continue;       // a config this build does not have
+        if (id < 0) continue;       // a config this library does not contain
         out.push_back({d, (char)std::tolower(a[0]), (char)std::tolower(b[0]),
                        (char)std::tolower(c[0]), M, N, K, id});
     }
