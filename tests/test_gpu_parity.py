@@ -619,6 +619,33 @@ def test_epilogue_stream_k_256_whole_and_split_tiles(dtype):
         log(f"{name}: 256 whole + 16 split tiles with epilogue exact")
 
 
+def test_epilogue_random_shapes_configs_exact():
+    """80 seeded random epilogue cases: M, N in [1, 600], K in [0, 600], any
+    layout, dtype and config (stream-K ones with a workspace), alpha and beta
+    from powers of two and zero, with or without a bias, relu or none.  Every
+    intermediate is exact in fp32 (|sum| <= 600 * 25), so the result must
+    match the oracle's epilogue bit for bit."""
+    import dense_gemm_engineering_run_amd as g
+    rng = np.random.Generator(np.random.PCG64(4242))
+    for case in range(80):
+        dtype = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"][rng.integers(5)]
+        code = gi.DTYPE_CODE[dtype]
+        M, N = (int(x) for x in rng.integers(1, 601, size=2))
+        K = int(rng.integers(0, 601))
+        layout = LAYOUTS8[rng.integers(8)]
+        cfg = int(rng.integers(g.gemm_num_configs(code)))
+        alpha = float(rng.choice([1.0, 2.0, -0.5, 0.25]))
+        beta = float(rng.choice([0.0, 1.0, -0.5, 2.0]))
+        act = int(rng.choice([g.GEMM_ACT_NONE, g.GEMM_ACT_RELU]))
+        with_bias = bool(rng.random() < 0.7)
+        log(f"case {case}: {dtype} {M}x{N}x{K} {''.join(layout)} {g.gemm_config_describe(code, cfg)} "
+            f"alpha={alpha} beta={beta} act={act} bias={with_bias}")
+        used = epi_case(M, N, K, layout, dtype, "int5", alpha, beta, act, with_bias=with_bias, config=cfg,
+                        seed=100 + case)
+        assert used == cfg or (M == 0 or N == 0)
+    log("80 random epilogue cases exact")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
 def test_epilogue_gelu_and_scale(dtype):
     import dense_gemm_engineering_run_amd as g
