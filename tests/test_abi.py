@@ -276,6 +276,33 @@ def test_tuning_table_lookup(tmp_path):
     assert g.gemm_tuning_size() == saved
 
 
+def test_committed_tuning_table_is_whole():
+    """Every line of the shipped table names a config the library has (the
+    loader skips unknown names, so a renamed config would otherwise drop its
+    keys silently), its keys are exactly those of keys.txt, and a key with two
+    lines is a stream-K winner followed by its no-workspace fallback."""
+    tdir = os.path.join(ROOT, "dense_gemm_engineering_run_amd", "tuning")
+    rows = [l.split("#")[0].split() for l in open(os.path.join(tdir, "table.txt"))]
+    rows = [r for r in rows if r]
+    keys = [l.split("#")[0].split() for l in open(os.path.join(tdir, "keys.txt"))]
+    keys = {" ".join(k) for k in keys if len(k) == 7}
+    saved = g.gemm_tuning_size()
+    try:
+        assert g.gemm_load_tuning(os.path.join(tdir, "table.txt")) == b.GEMM_OK
+        assert g.gemm_tuning_size() == len(rows)
+    finally:
+        g.gemm_load_tuning(b.DEFAULT_TABLE)
+    assert g.gemm_tuning_size() == saved
+    by_key = {}
+    for r in rows:
+        by_key.setdefault(" ".join(r[:7]), []).append(" ".join(r[7:]))
+    assert set(by_key) == keys
+    for k, cfgs in by_key.items():
+        assert len(cfgs) in (1, 2), k
+        if len(cfgs) == 2:
+            assert cfgs[0].endswith(" sk") and not cfgs[1].endswith(" sk"), (k, cfgs)
+
+
 def test_torch_helper_derives_majors_from_strides():
     torch = pytest.importorskip("torch")
     a = torch.empty(64, 40)                      # (M, K) row-major -> 'k', lda 40
