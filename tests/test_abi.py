@@ -316,6 +316,23 @@ def test_torch_helper_derives_majors_from_strides():
         b.dtype_code(torch.float64, torch.float64)
 
 
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """A copy of the package without libmi355_gemm.so must refuse to import
+    (no CPU or eager fallback exists to take over)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "dense_gemm_engineering_run_amd")
+    dst = tmp_path / "dense_gemm_engineering_run_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    assert not any(p.suffix == ".so" for p in dst.iterdir())
+    r = subprocess.run([sys.executable, "-c", "import dense_gemm_engineering_run_amd"], cwd=tmp_path,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)}, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libmi355_gemm.so is missing" in r.stderr, r.stderr[-2000:]
+
+
 def test_build_scripts_need_no_built_library():
     """__graft_entry__.build() must work on a fresh checkout, where the
     libraries do not exist yet: the build scripts load by path and import
