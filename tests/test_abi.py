@@ -248,6 +248,18 @@ def test_select_config_is_host_logic():
     assert g.gemm_select_config(1, 1, 1, "k", "k", "n", 9) == -b.GEMM_ERR_BAD_DTYPE
 
 
+def test_heuristic_for_large_untuned_16bit_shapes():
+    """Shapes far from every tuned key take the heuristic: the 256x256 tile on
+    16x16x32 MFMAs, except for fp32 outputs on grids of 512 or more of its
+    tiles, which keep the 32x32x16 form."""
+    def chosen(M, N, K, d):
+        return g.gemm_config_describe(d, g.gemm_select_config(M, N, K, "k", "k", "n", d))
+    assert chosen(16384, 16384, 1024, 3) == "f16_f16 256x256x64 w4x2 mfma16 s2 dma"
+    assert chosen(3008, 12000, 3008, 2) == "bf16_bf16 256x256x64 w4x2 mfma16 s2 dma"
+    assert chosen(16384, 16384, 1024, 1) == "f16_f32 256x256x64 w4x2 mfma32 s2 dma"
+    assert chosen(16384, 16384, 1024, 4) == "bf16_f32 256x256x64 w4x2 mfma32 s2 dma"
+
+
 def test_tuning_table_lookup(tmp_path):
     saved = g.gemm_tuning_size()
     name0 = g.gemm_config_describe(0, 0)

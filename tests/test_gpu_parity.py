@@ -387,11 +387,12 @@ def test_batched_direct_to_lds_kernels(dtype, layout):
 def test_batched_selection_counts_every_entry():
     """A strided batch is one launch over all its entries' tiles: 64 x 512^3
     and 16 x 1024^3 (whose batch-1 table entry names a 64x64 tile) both go to
-    the 256x256 direct-to-LDS kernel, and stay exact (sampled entries)."""
+    the 256x256 direct-to-LDS kernel (one wave of its tiles: the 16x16x32
+    form), and stay exact (sampled entries)."""
     import dense_gemm_engineering_run_amd as g
     for M, batch in ((512, 64), (1024, 16)):
         cfg = batched_case(M, M, 512, ("k", "k", "n"), "f16_f32", "int5", batch, rows=[(0, 64), (M - 64, M)])
-        assert g.gemm_config_describe(1, cfg) == "f16_f32 256x256x64 w4x2 mfma32 s2 dma", g.gemm_config_describe(1, cfg)
+        assert g.gemm_config_describe(1, cfg) == "f16_f32 256x256x64 w4x2 mfma16 s2 dma", g.gemm_config_describe(1, cfg)
     log("batched selection: 256x256 tile for 64 x 512^3 and 16 x 1024^3")
 
 
