@@ -258,6 +258,11 @@ def test_heuristic_for_large_untuned_16bit_shapes():
     assert chosen(3008, 12000, 3008, 2) == "bf16_bf16 256x256x64 w4x2 mfma16 s2 dma"
     assert chosen(16384, 16384, 1024, 1) == "f16_f32 256x256x64 w4x2 mfma32 s2 dma"
     assert chosen(16384, 16384, 1024, 4) == "bf16_f32 256x256x64 w4x2 mfma32 s2 dma"
+    # mid-size (64 to 191 tiles of 256x256): the 128x128 tile, on 16x16x32
+    # MFMAs only when both operands are k-contiguous
+    assert chosen(2560, 2560, 16384, 1) == "f16_f32 128x128x64 w2x2 mfma16 s4 dma"
+    sel = g.gemm_select_config(2560, 2560, 16384, "m", "n", "n", 1)
+    assert g.gemm_config_describe(1, sel) == "f16_f32 128x128x64 w2x2 mfma32 s4 dma"
 
 
 def test_tuning_table_lookup(tmp_path):
