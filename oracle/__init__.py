@@ -53,7 +53,8 @@ def gemm_ref(M, N, K, a_major, b_major, in_type, A, lda, B, ldb, rows=None, thre
     ``A`` and ``B`` are flat numpy storage arrays: float32 for ``in_type='f32'``,
     uint16 bit patterns for ``'f16'``/``'bf16'``.  Majors and leading dimensions
     follow the SGEMM example's convention ('k'/'m' for A, 'k'/'n' for B).
-    Returns a dense (end-begin) x N float64 array.
+    Returns a dense (end-begin) x N float64 array.  ``threads`` defaults to
+    every CPU this process may run on.
     """
     lib = _load()
     r0, r1 = (0, M) if rows is None else rows
@@ -62,7 +63,7 @@ def gemm_ref(M, N, K, a_major, b_major, in_type, A, lda, B, ldb, rows=None, thre
     B = np.ascontiguousarray(B, dtype=want)
     out = np.zeros((max(r1 - r0, 0), N), dtype=np.float64)
     if threads is None:
-        threads = os.cpu_count() or 1
+        threads = len(os.sched_getaffinity(0)) or 1
     rc = lib.oracle_gemm(M, N, K, a_major.encode(), b_major.encode(), IN_TYPES[in_type],
                          _ptr(A), lda, _ptr(B), ldb, r0, r1, _ptr(out), int(threads))
     if rc != 0:

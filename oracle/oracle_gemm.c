@@ -26,8 +26,9 @@
  * The result is returned as a dense row-major M x N array of doubles; the
  * caller rounds it to the output type with the oracle_round_* functions.
  *
- * Parallelism: rows of C are split evenly over POSIX threads.  This does not
- * change the sequence of operations of any element.
+ * Parallelism: rows of C are split evenly over POSIX threads, and each thread
+ * walks four columns of a row at a time.  Neither changes the sequence of
+ * operations of any element.
  */
 #include <math.h>
 #include <pthread.h>
@@ -86,14 +87,37 @@ typedef struct {
 static void* run_rows(void* arg)
 {
     const job_t* j = (const job_t*)arg;
+    const int64_t N = j->N, K = j->K;
     for (int64_t m = j->r_begin; m < j->r_end; ++m) {
-        const double* a = j->A + m * j->K;
-        for (int64_t n = 0; n < j->N; ++n) {
-            const double* b = j->B + n * j->K;
+        const double* a = j->A + m * K;
+        double* c = j->C + m * N;
+        int64_t n = 0;
+        /* Four columns side by side: four independent sums, each still one
+         * fp64 multiply and one fp64 add per k, k ascending. */
+        for (; n + 4 <= N; n += 4) {
+            const double* b0 = j->B + n * K;
+            const double* b1 = b0 + K;
+            const double* b2 = b1 + K;
+            const double* b3 = b2 + K;
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double x = a[k];
+                s0 = s0 + x * b0[k];
+                s1 = s1 + x * b1[k];
+                s2 = s2 + x * b2[k];
+                s3 = s3 + x * b3[k];
+            }
+            c[n] = s0;
+            c[n + 1] = s1;
+            c[n + 2] = s2;
+            c[n + 3] = s3;
+        }
+        for (; n < N; ++n) {
+            const double* b = j->B + n * K;
             double s = 0.0;
-            for (int64_t k = 0; k < j->K; ++k)
+            for (int64_t k = 0; k < K; ++k)
                 s = s + a[k] * b[k];
-            j->C[m * j->N + n] = s;
+            c[n] = s;
         }
     }
     return NULL;

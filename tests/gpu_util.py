@@ -95,15 +95,15 @@ def padding_intact(flat, prob):
     return bool(np.all(pad == s))
 
 
+def no_sentinel(c_logical, prob):
+    """True when no element of the logical C still holds the sentinel that
+    c_buffer() wrote (every element was stored)."""
+    bits = np.asarray(c_logical)
+    if prob["out_type"] == "f32":
+        return not bool(np.any(bits.view(np.uint32) == SENTINEL["f32"]))
+    return not bool(np.any(bits.view(np.uint16) == SENTINEL[prob["out_type"]]))
+
+
 def check(c_logical, ref, prob, exact, rows=None):
     sub = c_logical if rows is None else c_logical[rows[0]:rows[1]]
     return compare.check(sub, ref, prob["out_type"], exact)
-
-
-def sample_blocks(M, size=16, seed=0):
-    """Row blocks to compare at full size: the first and the last `size` rows
-    and one block at a seeded random position, as (begin, end) pairs."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    size = min(size, M)
-    mid = int(rng.integers(0, max(M - size, 0) + 1))
-    return sorted({(0, size), (mid, mid + size), (M - size, M)})

@@ -6,8 +6,9 @@ Workloads (seeded, synthetic; see gemm_inputs):
   3. fp16 4096^3 -> fp32, all 8 layouts, normal(0,1)                         -> normwise <= 1e-5
   4. fp32 4095x2049x1028 ragged, A k, B k, C n (ldc 2052), uniform(-1,1)     -> normwise <= 1e-5
   5. bf16 65536x256x4096 -> bf16, A k, B k, C n, normal(0,0.02)              -> normwise <= 8e-3
-Integer-valued inputs at each shape must match bit for bit.  Large shapes are
-compared on sampled row blocks (all columns), small ones in full.
+Integer-valued inputs at each shape must match bit for bit.  Every workload
+is compared with the oracle over the whole of C, every element; C starts
+filled with a NaN sentinel, so a tile that is never written fails the check.
 """
 import itertools
 import os
@@ -29,26 +30,17 @@ def log(msg):
     print(msg, flush=True)
 
 
-def full_check(prob, exact, config=None):
-    c, flat, st = gu.run(prob, config=config)
+def full_check(prob, exact, config=None, ref=None, dev=None):
+    """Run `prob` and compare all of C with the oracle (computed here unless
+    `ref` is given); C's ld padding must keep the sentinel."""
+    c, flat, st = gu.run(prob, config=config, dev=dev)
     assert st == 0, st
-    ref = gu.reference(prob)
+    if ref is None:
+        ref = gu.reference(prob)
+    assert gu.no_sentinel(c, prob), "C holds unwritten elements"
     ok, info = gu.check(c, ref, prob, exact)
     assert ok, info
     assert gu.padding_intact(flat, prob)
-    return info
-
-
-def sampled_check(prob, exact, dev=None, blocks=None, c=None):
-    if c is None:
-        c, flat, st = gu.run(prob, dev=dev)
-        assert st == 0, st
-        assert gu.padding_intact(flat, prob)
-    blocks = blocks or gu.sample_blocks(prob["M"])
-    refs = [gu.reference(prob, rows=b) for b in blocks]
-    got = np.concatenate([c[b0:b1] for b0, b1 in blocks])
-    ok, info = gu.check(got, np.concatenate(refs), prob, exact)
-    assert ok, (blocks, info)
     return info
 
 
@@ -64,7 +56,7 @@ def test_w1_fp32_1024x512x256_integer_exact():
 def test_w2_fp32_8192_cube(kind, exact):
     log(f"w2 fp32 8192^3 mnn {kind}")
     prob = gi.problem(8192, 8192, 8192, "m", "n", "n", "f32", kind)
-    info = sampled_check(prob, exact)
+    info = full_check(prob, exact)
     log(f"  {info}")
 
 
@@ -73,20 +65,15 @@ def test_w3_fp16_4096_cube_all_layouts(kind, exact):
     M = N = K = 4096
     a_log, b_log = gi.draw_ab(M, N, K, kind)
     a16, b16 = gi.cast(a_log, "f16"), gi.cast(b_log, "f16")
-    blocks = gu.sample_blocks(M)
-    refs = None
+    ref = None
     for am, bm, cm in LAYOUTS8:
         log(f"w3 fp16 4096^3 {am}{bm}{cm} {kind}")
         prob = dict(M=M, N=N, K=K, a_major=am, b_major=bm, c_major=cm, dtype=1, in_type="f16",
                     out_type="f32", lda=4096, ldb=4096, ldc=4096, c_first=(cm == "m"),
                     A=gi.store(a16, am == "m", 4096), B=gi.store(b16, bm == "n", 4096))
-        c, flat, st = gu.run(prob)
-        assert st == 0
-        if refs is None:  # same logical inputs for every layout: compute the oracle once
-            refs = np.concatenate([gu.reference(prob, rows=b) for b in blocks])
-        got = np.concatenate([c[b0:b1] for b0, b1 in blocks])
-        ok, info = gu.check(got, refs, prob, exact)
-        assert ok, (am, bm, cm, info)
+        if ref is None:  # same logical inputs for every layout: compute the oracle once
+            ref = gu.reference(prob)
+        info = full_check(prob, exact, ref=ref)
         log(f"  {info}")
 
 
@@ -102,7 +89,7 @@ def test_w4_fp32_ragged(kind, exact):
 def test_w5_bf16_tall_skinny(kind, exact):
     log(f"w5 bf16 65536x256x4096 kkn {kind}")
     prob = gi.problem(65536, 256, 4096, "k", "k", "n", "bf16_bf16", kind)
-    info = sampled_check(prob, exact, blocks=gu.sample_blocks(65536, size=64))
+    info = full_check(prob, exact)
     log(f"  {info}")
 
 
@@ -283,10 +270,10 @@ def test_graph_capture_and_replay():
 @pytest.mark.parametrize("K,kind,exact", [(512, "n01", False), (16384, "n01", False), (2048, "int5", True)])
 def test_fp16_out_sweep_8192(K, kind, exact):
     """M = N = 8192, fp16 in and out, A k-major, B n-major (B stored K x N
-    row-major), C n-major; sampled row blocks against the oracle rounded to fp16."""
+    row-major), C n-major; all of C against the oracle rounded to fp16."""
     log(f"sweep f16_f16 8192x8192x{K} knn {kind}")
     prob = gi.problem(8192, 8192, K, "k", "n", "n", "f16_f16", kind)
-    info = sampled_check(prob, exact, blocks=gu.sample_blocks(8192, size=8))
+    info = full_check(prob, exact)
     log(f"  {info}")
 
 
@@ -310,10 +297,10 @@ def _pack(arrs, shared):
     return buf, stride
 
 
-def batched_case(M, N, K, layout, dtype, kind, batch, share="", rows=None, seed=11):
+def batched_case(M, N, K, layout, dtype, kind, batch, share="", seed=11):
     """Run one strided-batched call and compare every entry with the oracle.
     share: "a" and/or "b" give that operand stride 0 (one matrix for all).
-    rows: row blocks to compare (None: all rows)."""
+    Every entry is compared in full."""
     import torch
     import dense_gemm_engineering_run_amd as g
     a_m, b_m, c_m = layout
@@ -343,11 +330,9 @@ def batched_case(M, N, K, layout, dtype, kind, batch, share="", rows=None, seed=
     sentinel = gu.SENTINEL[p0["out_type"]]
     for l, p in enumerate(probs):
         part = flat[l * sc: l * sc + outer * p["ldc"]]
-        got = gi.load(part, M, N, p["c_first"], p["ldc"])
-        blocks = rows or [(0, M)]
-        ref = np.concatenate([gu.reference(p, rows=b) for b in blocks])
-        sub = np.concatenate([got[b0:b1] for b0, b1 in blocks])
-        ok, info = gu.check(np.ascontiguousarray(sub), ref, p, kind == "int5")
+        got = np.ascontiguousarray(gi.load(part, M, N, p["c_first"], p["ldc"]))
+        assert gu.no_sentinel(got, p), l
+        ok, info = gu.check(got, gu.reference(p), p, kind == "int5")
         assert ok, (l, info)
         assert gu.padding_intact(part, p), l
         gap = flat[l * sc + outer * p["ldc"]: (l + 1) * sc] if l + 1 < batch else flat[:0]
@@ -374,11 +359,10 @@ def test_batched_broadcast_operand(share):
 @pytest.mark.parametrize("dtype,layout", [("f32", "mnn"), ("f32", "kkn"), ("f16_f32", "kkn"),
                                           ("f16_f32", "mnm"), ("bf16_bf16", "kkn")])
 def test_batched_direct_to_lds_kernels(dtype, layout):
-    """Shapes large enough for the direct-to-LDS kernels; sampled rows."""
+    """Shapes large enough for the direct-to-LDS kernels; every entry in full."""
     import dense_gemm_engineering_run_amd as g
     log(f"batched large {dtype} {layout}")
-    cfg = batched_case(4096, 4096, 104, tuple(layout), dtype, "int5", 2,
-                       rows=gu.sample_blocks(4096, size=8))
+    cfg = batched_case(4096, 4096, 104, tuple(layout), dtype, "int5", 2)
     name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
     log(f"  config {name}")
     assert name.endswith("dma"), name
@@ -388,10 +372,10 @@ def test_batched_selection_counts_every_entry():
     """A strided batch is one launch over all its entries' tiles: 64 x 512^3
     and 16 x 1024^3 (whose batch-1 table entry names a 64x64 tile) both go to
     the 256x256 direct-to-LDS kernel (one wave of its tiles: the 16x16x32
-    form), and stay exact (sampled entries)."""
+    form), and stay exact (every entry in full)."""
     import dense_gemm_engineering_run_amd as g
     for M, batch in ((512, 64), (1024, 16)):
-        cfg = batched_case(M, M, 512, ("k", "k", "n"), "f16_f32", "int5", batch, rows=[(0, 64), (M - 64, M)])
+        cfg = batched_case(M, M, 512, ("k", "k", "n"), "f16_f32", "int5", batch)
         assert g.gemm_config_describe(1, cfg) == "f16_f32 256x256x64 w4x2 mfma16 s2 dma", g.gemm_config_describe(1, cfg)
     log("batched selection: 256x256 tile for 64 x 512^3 and 16 x 1024^3")
 
@@ -420,10 +404,10 @@ def _sk_configs(dtype="f32"):
     return [i for i in range(g.gemm_num_configs(code)) if g.gemm_config_describe(code, i).endswith(" sk")]
 
 
-def sk_case(M, N, K, layout, config, kind, ldc=None, rows=None, seed=5, dtype="f32"):
+def sk_case(M, N, K, layout, config, kind, ldc=None, seed=5, dtype="f32", ref=None):
     """Run a stream-K config through gemm_run_ws twice (fresh C each time) and
-    compare with the oracle; the second run also checks that the first left
-    the workspace's arrival counters at zero."""
+    compare all of C with the oracle (`ref` if given); the second run also
+    checks that the first left the workspace's arrival counters at zero."""
     import torch
     import dense_gemm_engineering_run_amd as g
     code = gi.DTYPE_CODE[dtype]
@@ -445,10 +429,10 @@ def sk_case(M, N, K, layout, config, kind, ldc=None, rows=None, seed=5, dtype="f
     (c0, f0), (c1, f1) = outs
     assert np.array_equal(f0.view(np.uint8), f1.view(np.uint8)), "not deterministic"
     assert gu.padding_intact(f0, prob)
-    blocks = rows or [(0, M)]
-    refs = np.concatenate([gu.reference(prob, rows=bk) for bk in blocks])
-    got = np.concatenate([c0[b0:b1] for b0, b1 in blocks])
-    ok, info = gu.check(got, refs, prob, kind == "int5")
+    assert gu.no_sentinel(c0, prob), "C holds unwritten elements"
+    if ref is None:
+        ref = gu.reference(prob)
+    ok, info = gu.check(c0, ref, prob, kind == "int5")
     assert ok, info
     return need, info
 
@@ -469,13 +453,12 @@ def test_stream_k_every_config_every_layout(dtype):
 @pytest.mark.parametrize("kind,exact", [("int5", True), ("u11", False)])
 def test_stream_k_ragged_workload(kind, exact):
     """4095x2049x1028, A k, B k, C n with ldc 2052: 144 tiles of 256x256 over
-    256 workgroups; sampled row blocks."""
+    256 workgroups; all of C."""
     import dense_gemm_engineering_run_amd as g
-    rows = gu.sample_blocks(4095, size=8, seed=1) + gu.sample_blocks(4095, size=8, seed=2)
-    rows = sorted(set(rows))
+    ref = gu.reference(gi.problem(4095, 2049, 1028, "k", "k", "n", "f32", kind, seed=5, ldc=2052))
     for cfg in _sk_configs():
         log(f"stream-K ragged {g.gemm_config_describe(0, cfg)} {kind}")
-        sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2052, rows=rows)
+        sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2052, ref=ref)
 
 
 @pytest.mark.parametrize("dtype", SK_DTYPES)
@@ -490,7 +473,7 @@ def test_stream_k_data_parallel_waves_plus_split_tail(dtype):
         name = g.gemm_config_describe(code, cfg)
         M, N = (6144, 5888) if " 256x256x" in name else (4352, 4352)
         log(f"stream-K dp+sk {name} {M}x{N}x96")
-        sk_case(M, N, 96, ("k", "n", "n"), cfg, "int5", rows=gu.sample_blocks(M, size=8, seed=3), dtype=dtype)
+        sk_case(M, N, 96, ("k", "n", "n"), cfg, "int5", dtype=dtype)
 
 
 @pytest.mark.parametrize("dtype,kind", [("f16_f32", "n01"), ("bf16_bf16", "n002"), ("f16_f16", "int5")])
@@ -499,17 +482,17 @@ def test_stream_k_16bit_ragged(dtype, kind):
     k-tile (a zero-filled partial last k-tile inside split ranges)."""
     import dense_gemm_engineering_run_amd as g
     code = gi.DTYPE_CODE[dtype]
-    rows = sorted(set(gu.sample_blocks(4095, size=8, seed=4)))
+    ref = gu.reference(gi.problem(4095, 2049, 1028, "k", "k", "n", dtype, kind, seed=5, ldc=2056))
     for cfg in _sk_configs(dtype):
         log(f"stream-K ragged {g.gemm_config_describe(code, cfg)} {kind}")
-        sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2056, rows=rows, dtype=dtype)
+        sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2056, dtype=dtype, ref=ref)
 
 
 def test_stream_k_whole_waves_and_k_zero_need_no_workspace():
     import dense_gemm_engineering_run_amd as g
     cfg = _sk_configs()[0]
     assert g.gemm_config_describe(0, cfg).startswith("f32 256x256")
-    need, _ = sk_case(4096, 4096, 64, ("k", "k", "n"), cfg, "int5", rows=gu.sample_blocks(4096, 8))
+    need, _ = sk_case(4096, 4096, 64, ("k", "k", "n"), cfg, "int5")
     assert need == 0
     need, _ = sk_case(700, 300, 0, ("k", "k", "n"), cfg, "int5")
     assert need == 0

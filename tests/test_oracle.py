@@ -105,6 +105,29 @@ def test_exact_within_rounding_bound_noninteger():
                 assert abs(Fraction(float(got[m, n])) - exact[m][n]) <= Fraction(bound)
 
 
+def test_sequential_fp64_sum_bitwise():
+    """Every element is one fp64 sum over k ascending, multiply and add as
+    separate IEEE operations: a Python loop over floats (IEEE doubles, one
+    rounding per operation) gives the same bits.  N = 11 and 6 leave column
+    remainders after the oracle's groups of four."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    for M, N, K, kind in [(5, 11, 67, "u11"), (3, 6, 130, "n01"), (2, 9, 1, "u11")]:
+        a = gi.draw(rng, M, K, kind)
+        b = gi.draw(rng, N, K, kind)
+        got = _oracle_logical(a, b, "k", "n", threads=2)
+        for m in range(M):
+            for n in range(N):
+                s = 0.0
+                for k in range(K):
+                    s = s + float(a[m, k]) * float(b[n, k])
+                assert got[m, n] == s, (M, N, K, m, n)
+    # k ascending: 1 + 2^-61 rounds to 1, then -1 cancels it (a sum that adds
+    # the first and last terms first keeps the 2^-61).
+    a = np.array([[1.0, 2.0 ** -30, -1.0]], dtype=np.float32)
+    b = np.array([[1.0, 2.0 ** -31, 1.0]] * 5, dtype=np.float32)
+    assert np.all(_oracle_logical(a, b) == 0.0)
+
+
 # ---------------------------------------------------------------- closed forms
 
 def test_closed_forms():
