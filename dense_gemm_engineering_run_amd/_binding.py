@@ -87,10 +87,20 @@ _lib.gemm_tuning_size.restype = _int
 DTYPE_F32, DTYPE_F16_F32, DTYPE_BF16_BF16, DTYPE_F16_F16, DTYPE_BF16_F32 = range(5)
 DTYPE_NAMES = ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"]
 
-# gemm_status_t
-(GEMM_OK, GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR, GEMM_ERR_BAD_DTYPE, GEMM_ERR_BAD_LD,
- GEMM_ERR_NULL_PTR, GEMM_ERR_MISALIGNED, GEMM_ERR_ALIAS, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP,
- GEMM_ERR_TUNING_FILE, GEMM_ERR_BAD_EPILOGUE, GEMM_ERR_WORKSPACE) = range(13)
+# gemm_status_t (values as in include/mi355_gemm.h)
+GEMM_OK = 0
+GEMM_ERR_NULL_PTR = 1
+GEMM_ERR_BAD_SHAPE = 2
+GEMM_ERR_BAD_MAJOR = 3
+GEMM_ERR_BAD_DTYPE = 4
+GEMM_ERR_BAD_LD = 5
+GEMM_ERR_MISALIGNED = 6
+GEMM_ERR_ALIAS = 7
+GEMM_ERR_NO_CONFIG = 8
+GEMM_ERR_HIP = 9
+GEMM_ERR_TUNING_FILE = 10
+GEMM_ERR_BAD_EPILOGUE = 11
+GEMM_ERR_WORKSPACE = 12
 
 # gemm_activation_t
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU = range(3)

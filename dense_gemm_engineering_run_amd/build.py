@@ -44,8 +44,20 @@ def _spills(remarks):
     return bad
 
 
-def _compile(src, verbose):
+def _fresh(src, obj):
+    """True when obj is newer than src and than every header it may include."""
+    if not os.path.exists(obj):
+        return False
+    deps = [src] + glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(CSRC, "*.def")) + \
+        glob.glob(os.path.join(ROOT, "include", "*.h"))
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(d) < t for d in deps)
+
+
+def _compile(src, verbose, incremental=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and _fresh(src, obj):
+        return obj
     cmd = [HIPCC, "-x", "hip", *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -61,12 +73,14 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, jobs=None, incremental=False):
+    """Compile every source (incremental: only those whose object is older
+    than the source or a header) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -77,4 +91,4 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv)

@@ -42,8 +42,12 @@
  * caller's synchronisation.
  *
  * Errors.  Every function returns a status and never throws.  All argument
- * checks run before any HIP call, in the order of gemm_status_t below, so
- * they can be exercised without a GPU.
+ * checks run before any HIP call, so they can be exercised without a GPU, in
+ * this order: shape (GEMM_ERR_BAD_SHAPE), majors (BAD_MAJOR), dtype
+ * (BAD_DTYPE), leading dimensions and batch strides (BAD_LD), pointers
+ * (NULL_PTR), alignment (MISALIGNED), overlap (ALIAS), then the config
+ * (NO_CONFIG), the epilogue (BAD_EPILOGUE) and the workspace (WORKSPACE).
+ * The first failing check decides the status.
  *
  * Degenerate sizes.  M == 0 or N == 0: nothing is launched, GEMM_OK.
  * K == 0: C is filled with zeros (the empty sum); A and B are not read.
@@ -73,11 +77,11 @@ typedef enum {
 
 typedef enum {
     GEMM_OK = 0,
-    GEMM_ERR_BAD_SHAPE = 1,    /* M, N, K or batch negative, or too large for the tile indexing */
-    GEMM_ERR_BAD_MAJOR = 2,    /* major character not in {k,m} / {k,n} / {n,m}          */
-    GEMM_ERR_BAD_DTYPE = 3,    /* dtype not a gemm_dtype_t                               */
-    GEMM_ERR_BAD_LD = 4,       /* ld below the contiguous extent (or 1); bad batch stride */
-    GEMM_ERR_NULL_PTR = 5,     /* A or B NULL while M*N*K > 0, or C NULL while M*N > 0   */
+    GEMM_ERR_NULL_PTR = 1,     /* A or B NULL while M*N*K > 0, or C NULL while M*N > 0   */
+    GEMM_ERR_BAD_SHAPE = 2,    /* M, N, K or batch negative, or too large for the tile indexing */
+    GEMM_ERR_BAD_MAJOR = 3,    /* major character not in {k,m} / {k,n} / {n,m}          */
+    GEMM_ERR_BAD_DTYPE = 4,    /* dtype not a gemm_dtype_t                               */
+    GEMM_ERR_BAD_LD = 5,       /* ld below the contiguous extent (or 1); bad batch stride */
     GEMM_ERR_MISALIGNED = 6,   /* pointer not element-aligned (workspace: 16 bytes), or a
                                   forced config that needs 16-byte alignment the operands lack */
     GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */

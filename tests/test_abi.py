@@ -31,8 +31,37 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+# Status values of the boundary: success 0, then the argument errors in the
+# order null pointer, shape, major, dtype, leading dimension, alignment,
+# aliasing, config, launch; the library's own additions follow.
+STATUS_VALUES = {
+    "GEMM_OK": 0, "GEMM_ERR_NULL_PTR": 1, "GEMM_ERR_BAD_SHAPE": 2, "GEMM_ERR_BAD_MAJOR": 3,
+    "GEMM_ERR_BAD_DTYPE": 4, "GEMM_ERR_BAD_LD": 5, "GEMM_ERR_MISALIGNED": 6, "GEMM_ERR_ALIAS": 7,
+    "GEMM_ERR_NO_CONFIG": 8, "GEMM_ERR_HIP": 9, "GEMM_ERR_TUNING_FILE": 10,
+    "GEMM_ERR_BAD_EPILOGUE": 11, "GEMM_ERR_WORKSPACE": 12,
+}
+
+
+def header_enum(name):
+    """{enumerator: value} of the typedef enum `name` in the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum \{([^}]*)\}\s*" + name + ";", text).group(1)
+    return {k: int(v) for k, v in re.findall(r"(\w+)\s*=\s*(\d+)", body)}
+
+
+def test_status_values_pinned_in_header_and_binding():
+    assert header_enum("gemm_status_t") == STATUS_VALUES
+    for k, v in STATUS_VALUES.items():
+        assert getattr(b, k) == v, k
+    assert header_enum("gemm_dtype_t") == {"GEMM_DTYPE_F32": 0, "GEMM_DTYPE_F16_F32": 1,
+                                           "GEMM_DTYPE_BF16_BF16": 2, "GEMM_DTYPE_F16_F16": 3,
+                                           "GEMM_DTYPE_BF16_F32": 4, "GEMM_NUM_DTYPES": 5}
+    assert header_enum("gemm_activation_t") == {"GEMM_ACT_NONE": 0, "GEMM_ACT_RELU": 1, "GEMM_ACT_GELU": 2}
+    assert (b.GEMM_ACT_NONE, b.GEMM_ACT_RELU, b.GEMM_ACT_GELU) == (0, 1, 2)
+
+
 def test_status_strings():
-    for st in range(13):
+    for st in range(len(STATUS_VALUES)):
         s = g.gemm_status_str(st)
         assert s and s != "unknown status"
     assert g.gemm_status_str(99) == "unknown status"
