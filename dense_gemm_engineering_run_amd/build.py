@@ -44,14 +44,24 @@ def _spills(remarks):
     return bad
 
 
+def _includes(path, seen):
+    """Local headers that `path` includes, transitively (quoted #includes
+    found in csrc/ or include/)."""
+    for name in re.findall(r'^\s*#\s*include\s+"([^"]+)"', open(path).read(), flags=re.M):
+        for d in (CSRC, os.path.join(ROOT, "include")):
+            h = os.path.join(d, name)
+            if os.path.exists(h) and h not in seen:
+                seen.add(h)
+                _includes(h, seen)
+    return seen
+
+
 def _fresh(src, obj):
-    """True when obj is newer than src and than every header it may include."""
+    """True when obj is newer than src and than every local header it includes."""
     if not os.path.exists(obj):
         return False
-    deps = [src] + glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(CSRC, "*.def")) + \
-        glob.glob(os.path.join(ROOT, "include", "*.h"))
     t = os.path.getmtime(obj)
-    return all(os.path.getmtime(d) < t for d in deps)
+    return all(os.path.getmtime(d) < t for d in [src, *_includes(src, set())])
 
 
 def _compile(src, verbose, incremental=False):
