@@ -60,6 +60,8 @@ _lib.gemm_run_batched.argtypes = _RUN_ARGS[:-1] + [_i64, _i64, _i64, _i64, _vp]
 _lib.gemm_run_batched.restype = _int
 _lib.gemm_run_ws.argtypes = _RUN_ARGS[:-1] + [_vp, ctypes.c_size_t, _vp, _int]
 _lib.gemm_run_ws.restype = _int
+_lib.gemm_run_noalloc.argtypes = _RUN_ARGS + [_int]
+_lib.gemm_run_noalloc.restype = _int
 _lib.gemm_run_ex.argtypes = _RUN_ARGS[:-1] + [ctypes.POINTER(Epilogue), _vp, ctypes.c_size_t, _vp,
                                               _int]
 _lib.gemm_run_ex.restype = _int
@@ -101,6 +103,10 @@ GEMM_ERR_HIP = 9
 GEMM_ERR_TUNING_FILE = 10
 GEMM_ERR_BAD_EPILOGUE = 11
 GEMM_ERR_WORKSPACE = 12
+GEMM_ERR_SCRATCH_LIMIT = 13
+
+# bytes of the device scratch array behind gemm_run_noalloc
+GEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # gemm_activation_t
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU = range(3)
@@ -128,6 +134,13 @@ def gemm_run_batched(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ld
     """C ABI gemm_run_batched (strides in elements). Returns the status."""
     return _lib.gemm_run_batched(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
                                  lda, ldb, ldc, batch, stride_a, stride_b, stride_c, stream)
+
+
+def gemm_run_noalloc(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, stream=0,
+                     config_id=-1):
+    """C ABI gemm_run_noalloc (the library's own device scratch as workspace). Returns the status."""
+    return _lib.gemm_run_noalloc(M, N, K, _c(a_major), _c(b_major), _c(c_major), dtype, A, B, C,
+                                 lda, ldb, ldc, stream, config_id)
 
 
 def gemm_run_ws(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, workspace,

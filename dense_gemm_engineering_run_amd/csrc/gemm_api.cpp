@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "gemm_kernel.hpp"
+#include "gemm_plan.hpp"
 
 namespace {
 
@@ -532,6 +533,41 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
 
 }  // namespace
 
+namespace mg {
+
+int plan_ws(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
+            const void* B, const void* C, int64_t lda, int64_t ldb, int64_t ldc, size_t ws_bytes,
+            int config_id, int* config, uint64_t* need, uint64_t* count_bytes)
+{
+    *config = -1;
+    *need = *count_bytes = 0;
+    bool vec16 = true;
+    int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, 1, 0, 0, 0, nullptr, 0, nullptr, &vec16);
+    if (st != GEMM_OK) return st;
+    int n = 0;
+    const KernelEntry* all = entries(dtype, &n);
+    if (config_id >= 0) {
+        if (config_id >= n) return GEMM_ERR_NO_CONFIG;
+        if (!vec16 && !is_scalar(dtype, config_id)) return GEMM_ERR_MISALIGNED;
+    }
+    if (M == 0 || N == 0) return GEMM_OK;
+    const int cfg = config_id >= 0 ? config_id : select_for(dtype, a, b, c, M, N, K, 1, ws_bytes, vec16);
+    if (cfg < 0) return GEMM_ERR_NO_CONFIG;
+    const bool swap = c == 'm';
+    const KernelEntry& e = all[cfg];
+    *config = cfg;
+    if (e.sk_occ > 0) {
+        const int64_t cm = swap ? N : M, cn = swap ? M : N;
+        const SkPlan sp = sk_plan(e, ((cm + e.BM - 1) / e.BM) * ((cn + e.BN - 1) / e.BN), (K + e.BK - 1) / e.BK);
+        if (!sp.ok) return GEMM_ERR_BAD_SHAPE;
+        *need = sp.bytes;
+        *count_bytes = sp.count_bytes;
+    }
+    return GEMM_OK;
+}
+
+}  // namespace mg
+
 extern "C" {
 
 int gemm_run(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major, int dtype,
@@ -615,6 +651,8 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
     case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
     case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation";
+    case GEMM_ERR_SCRATCH_LIMIT:
+        return "the config needs more workspace than the allocation-free entry point's fixed scratch (64 MiB)";
     default: return "unknown status";
     }
 }

@@ -21,7 +21,8 @@
  *     c_major 'n': C[m][n] at C + m*ldc + n     'm': at C + m + n*ldc
  * Major characters are case-insensitive.  Leading dimensions and sizes are in
  * ELEMENTS.  All pointers are device pointers (HBM), owned by the caller; the
- * library keeps no pointer after a call returns and allocates nothing.
+ * library keeps no pointer after a call returns and allocates nothing (the
+ * one device array it owns, for gemm_run_noalloc, is described there).
  *
  * Alignment (SGEMM example, "Constraints" in its docstring: the contiguous
  * dimension must be at least 16-byte aligned for its vectorised copies, and
@@ -53,7 +54,9 @@
  * K == 0: C is filled with zeros (the empty sum); A and B are not read.
  *
  * Threads.  All functions are reentrant.  The only global state is the tuning
- * table, guarded by a mutex, and a per-thread record of the last config.
+ * table, guarded by a mutex, a per-thread record of the last config, and the
+ * device scratch array of gemm_run_noalloc (whose calls on one GPU must not
+ * overlap).
  */
 #ifndef MI355_GEMM_H
 #define MI355_GEMM_H
@@ -89,7 +92,9 @@ typedef enum {
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
     GEMM_ERR_TUNING_FILE = 10, /* tuning table missing or malformed                      */
     GEMM_ERR_BAD_EPILOGUE = 11, /* unknown epilogue activation                              */
-    GEMM_ERR_WORKSPACE = 12    /* stream-K config without a large enough workspace       */
+    GEMM_ERR_WORKSPACE = 12,   /* stream-K config without a large enough workspace       */
+    GEMM_ERR_SCRATCH_LIMIT = 13 /* gemm_run_noalloc: the forced config needs more workspace
+                                   than the library's fixed scratch holds               */
 } gemm_status_t;
 
 /* Activations of the elementwise epilogue. */
@@ -186,6 +191,30 @@ int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, cha
                 int dtype, const void* A, const void* B, void* C,
                 int64_t lda, int64_t ldb, int64_t ldc, const gemm_epilogue_t* epilogue,
                 void* workspace, size_t workspace_bytes, void* stream, int config_id);
+
+/*
+ * For callers that cannot allocate device memory or call hipMalloc (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * gemm_run_ws with the workspace taken from a fixed array that the library
+ * owns in device memory, GEMM_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it
+ * runs on, held from the first call on that GPU until the process ends.
+ * Nothing is allocated per call; the caller passes A, B, C and the stream as
+ * for gemm_run_ws.  config_id < 0 chooses as gemm_run_ws does with a
+ * workspace of that size (a stream-K config only when it fits); a forced
+ * config that needs more returns GEMM_ERR_SCRATCH_LIMIT.  When the config is
+ * a stream-K one, a small kernel on `stream` first zeroes the arrival
+ * counters, then the GEMM runs.  The array is the GPU's (the stream's
+ * device; the current device for a NULL stream): every call on one GPU
+ * shares it and it keeps the last call's partial tiles, so calls that may
+ * overlap on one GPU (different streams, or host threads) race and must not
+ * be issued.  The first call on a GPU looks up the array's device address
+ * (GEMM_ERR_HIP if that fails).  Results equal gemm_run_ws's for the same
+ * config bit for bit.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
+                     int dtype, const void* A, const void* B, void* C,
+                     int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config_id);
 
 /*
  * Bytes of workspace that gemm_run_ws needs for this problem with config

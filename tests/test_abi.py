@@ -38,7 +38,7 @@ STATUS_VALUES = {
     "GEMM_OK": 0, "GEMM_ERR_NULL_PTR": 1, "GEMM_ERR_BAD_SHAPE": 2, "GEMM_ERR_BAD_MAJOR": 3,
     "GEMM_ERR_BAD_DTYPE": 4, "GEMM_ERR_BAD_LD": 5, "GEMM_ERR_MISALIGNED": 6, "GEMM_ERR_ALIAS": 7,
     "GEMM_ERR_NO_CONFIG": 8, "GEMM_ERR_HIP": 9, "GEMM_ERR_TUNING_FILE": 10,
-    "GEMM_ERR_BAD_EPILOGUE": 11, "GEMM_ERR_WORKSPACE": 12,
+    "GEMM_ERR_BAD_EPILOGUE": 11, "GEMM_ERR_WORKSPACE": 12, "GEMM_ERR_SCRATCH_LIMIT": 13,
 }
 
 
@@ -401,3 +401,33 @@ def test_build_scripts_need_no_built_library():
     import sys
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
+
+
+def test_noalloc_entry_point_host_checks():
+    """gemm_run_noalloc validates like gemm_run_ws before any HIP call; a
+    forced config that needs more workspace than the fixed scratch is refused
+    with its own status; an empty problem is a no-op."""
+    text = open(HEADER).read()
+    m = re.search(r"#define GEMM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == b.GEMM_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+    def na(M=64, N=64, K=64, A=P, B=2 * P, C=3 * P, cfg=-1, **kw):
+        return g.gemm_run_noalloc(M, N, K, "k", "k", "n", kw.get("dtype", 0), A, B, C,
+                                  kw.get("lda", K), kw.get("ldb", K), kw.get("ldc", N), 0, cfg)
+    assert na(M=-1) == b.GEMM_ERR_BAD_SHAPE
+    assert na(A=NULL) == b.GEMM_ERR_NULL_PTR
+    assert na(lda=3) == b.GEMM_ERR_BAD_LD
+    assert na(C=P + 16) == b.GEMM_ERR_ALIAS
+    assert na(cfg=10 ** 6) == b.GEMM_ERR_NO_CONFIG
+    assert na(M=0) == b.GEMM_OK and g.gemm_last_config() == -1
+    # the 256x256 fp32 stream-K tile on 24 x 23 tiles with a long K splits 40
+    # tiles over 256 workgroups: 128 MiB of partial tiles
+    sk = next(i for i in range(g.gemm_num_configs(0))
+              if g.gemm_config_describe(0, i) == "f32 256x256x32 w2x2 mfma32 s2 dma sk")
+    M, N, K = 6144, 5888, 8192
+    need = g.gemm_workspace_size(M, N, K, "k", "k", "n", 0, sk)
+    assert need > b.GEMM_NOALLOC_SCRATCH_BYTES
+    big = 1 << 34
+    st = g.gemm_run_noalloc(M, N, K, "k", "k", "n", 0, big, 2 * big, 3 * big, K, K, N, 0, sk)
+    assert st == b.GEMM_ERR_SCRATCH_LIMIT, g.gemm_status_str(st)
+    assert "scratch" in g.gemm_status_str(st)
