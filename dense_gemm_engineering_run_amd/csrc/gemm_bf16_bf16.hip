@@ -23,9 +23,15 @@ namespace mg {
     {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2 swz scalar",              \
      BM, BN, BK, WM, WN, MI, true, &Inst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, true, false>::launch, 2, false, 0, true},
 
+#define MG_DMA2_ENTRY(BM, BN, BK, WM, WN, MI, SA, SB)                                  \
+    {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s" #SA "x" #SB " dma",        \
+     BM, BN, BK, WM, WN, MI, true,                                                  \
+     &DmaInst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, SA, SB>::launch, SA, true},
+
 static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)
                                            MG_DMA_SK_CONFIGS_16(MG_DMA_SK_ENTRY)
-                                           MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)};
+                                           MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)
+                                               MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)};
 
 const KernelEntry* entries_bf16_bf16(int* n)
 {

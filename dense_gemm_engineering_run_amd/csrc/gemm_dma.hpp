@@ -8,7 +8,8 @@
 //    into LDS at (M0 + 16 * lane), with no VGPR staging and no LDS write
 //    instruction.  Bounds checking of the buffer resource writes zeros for
 //    out-of-range lanes.  The loads of one k-tile for both operands are issued
-//    STAGES-1 tiles ahead into a ring of STAGES LDS buffers (the multistage
+//    STAGES-1 tiles ahead into a ring of STAGES LDS buffers (or, for A, two
+//    tiles ahead into 3 buffers while B uses 2; the multistage
 //    shared-memory pipeline of the SGEMM example, mainloop comment), so several
 //    hundred KB per CU are in flight and the one barrier per k-tile both
 //    publishes tile t and frees the stage that tile t-1 used.
@@ -183,7 +184,12 @@ struct DmaOperand {
 // The pieces of the kernel: the main loop over a range of k-tiles of one C
 // tile, and the ways to store the tile (so that the persistent stream-K
 // kernel can run partial k-ranges with the same loop).
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM>
+// STAGES: depth of the A ring; SBS: depth of the B ring (the same, or one
+// less with two B stages: A, streamed from HBM, is then issued two k-tiles
+// ahead and B, read from the caches, one; the 2 MB B panel of a tall-skinny
+// problem stays in L2 while A needs every byte in flight that LDS can hold).
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM,
+          int SBS = STAGES>
 struct Dma16 {
     static_assert(TI != In::F32, "direct-to-LDS kernel is for 16-bit inputs");
     static constexpr int TILE_M = BM, TILE_N = BN, TILE_K = BK;
@@ -196,15 +202,35 @@ struct Dma16 {
     static constexpr int R = MI == 32 ? 16 : 4;        // accumulators per MFMA tile and lane
     using OA = DmaOperand<BM, BK, NW, AK>;
     using OB = DmaOperand<BN, BK, NW, BKM>;
+    static constexpr int SA = STAGES, SB = SBS;        // ring depths
+    static constexpr int DA = SA - 1, DB = SB - 1;     // k-tiles issued ahead
+    static_assert(SA == SB || (SA == 3 && SB == 2), "A ring as deep as B's, or 3 A and 2 B stages");
     static constexpr int STAGE = OA::BYTES + OB::BYTES;
     static constexpr int LPT = OA::IPW + OB::IPW;      // loads per wave per tile
-    static constexpr int SMEM = STAGES * STAGE;
+    static constexpr int SMEM = SA * OA::BYTES + SB * OB::BYTES;
+    // Loads issued after tile t's B loads (each k-tile issues B first, then
+    // A): those may still be in flight when tile t is waited for.
+    static constexpr int WAIT = (DA == DB ? 0 : OA::IPW) + (DB - 1) * LPT;
     static_assert(BK % KG == 0, "BK must be a multiple of the MFMA k");
-    static_assert(STAGES >= 2 && SMEM <= 160 * 1024, "LDS budget");
-    static_assert(LPT * (STAGES - 2) < 64, "vmcnt range");
+    static_assert(SB >= 2 && SMEM <= 160 * 1024, "LDS budget");
+    static_assert(WAIT < 64, "vmcnt range");
     using AccT = typename std::conditional<MI == 32, f32x16, f32x4>::type;
     typedef AccT Acc[TM][TN];
     static constexpr int PART_BYTES = BM * BN * 4;     // one partial tile, fp32 row-major
+
+    // LDS of k-tile i (counted from the first tile of a range) of each
+    // operand: with equal rings, stage i mod SA holds A then B; otherwise the
+    // A ring comes first and the B ring after it.
+    __device__ static __forceinline__ char* a_stage(char* smem, int i)
+    {
+        if constexpr (SA == SB) return smem + (i % SA) * STAGE;
+        else return smem + (i % SA) * OA::BYTES;
+    }
+    __device__ static __forceinline__ char* b_stage(char* smem, int i)
+    {
+        if constexpr (SA == SB) return smem + (i % SB) * STAGE + OA::BYTES;
+        else return smem + SA * OA::BYTES + (i % SB) * OB::BYTES;
+    }
 
     __device__ static __forceinline__ void zero(Acc& acc)
     {
@@ -238,29 +264,39 @@ struct Dma16 {
         const uint64_t a_bytes = p.a_bytes, b_bytes = p.b_bytes;
         const int64_t lda = p.lda, ldb = p.ldb;
 
-        // Every k-tile issues the loads of the tile STAGES-1 ahead, also past
-        // the end of the range: those get an empty extent (num_records 0)
-        // and write zeros into a stage that no later tile reads.  No branch
-        // precedes each k-group's loads, and the number of loads in flight is
-        // the same for every tile.
+        // Every k-tile issues the loads of the tiles DA (A) and DB (B) ahead,
+        // also past the end of the range: those get an empty extent
+        // (num_records 0) and write zeros into a stage that no later tile
+        // reads.  No branch precedes each k-group's loads, and the number of
+        // loads in flight is the same for every tile.
+        if constexpr (DA == DB) {
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) {
-            const bool live = kt0 + s < kt1;
-            char* st = smem + s * STAGE;
-            oa.issue(A, live ? a_bytes : 0, lda, m0, (kt0 + s) * BK, st, wave);
-            ob.issue(B, live ? b_bytes : 0, ldb, n0, (kt0 + s) * BK, st + OA::BYTES, wave);
+            for (int s = 0; s < DA; ++s) {
+                const bool live = kt0 + s < kt1;
+                oa.issue(A, live ? a_bytes : 0, lda, m0, (kt0 + s) * BK, a_stage(smem, s), wave);
+                ob.issue(B, live ? b_bytes : 0, ldb, n0, (kt0 + s) * BK, b_stage(smem, s), wave);
+            }
+        } else {
+            // A one tile further ahead: A(0), then B(s), A(s + 1) as the loop does.
+            oa.issue(A, kt0 < kt1 ? a_bytes : 0, lda, m0, kt0 * BK, a_stage(smem, 0), wave);
+#pragma unroll
+            for (int s = 0; s < DB; ++s) {
+                ob.issue(B, kt0 + s < kt1 ? b_bytes : 0, ldb, n0, (kt0 + s) * BK, b_stage(smem, s), wave);
+                oa.issue(A, kt0 + s + 1 < kt1 ? a_bytes : 0, lda, m0, (kt0 + s + 1) * BK, a_stage(smem, s + 1), wave);
+            }
         }
 
         for (int t = kt0; t < kt1; ++t) {
             const int r = t - kt0;
-            // Tile t has landed once the STAGES-2 later tiles' loads are all
-            // that remain outstanding.
-            wait_vmcnt<LPT * (STAGES - 2)>();
-            char* st = smem + (r % STAGES) * STAGE;
+            // Tile t has landed once the loads issued after its B loads are
+            // all that remain outstanding.
+            wait_vmcnt<WAIT>();
+            char* sa = a_stage(smem, r);
+            char* sb = b_stage(smem, r);
             if (t == nkt - 1 && ragged && (AK || BKM)) {
                 bare_barrier();
-                oa.template zero_tail<NT>(st, kvalid_last, tid);
-                ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+                oa.template zero_tail<NT>(sa, kvalid_last, tid);
+                ob.template zero_tail<NT>(sb, kvalid_last, tid);
                 __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
             }
             // A bare barrier: this wave's loads of tile t are complete (the vmcnt
@@ -268,13 +304,11 @@ struct Dma16 {
             // fenced __syncthreads() would also wait for the later tiles still in
             // flight.
             bare_barrier();
-            const bool more = t + STAGES - 1 < kt1;
-            const uint64_t na = more ? a_bytes : 0, nb = more ? b_bytes : 0;
-            char* nst = smem + ((r + STAGES - 1) % STAGES) * STAGE;
-            const int nk0 = (t + STAGES - 1) * BK;
+            const uint64_t na = t + DA < kt1 ? a_bytes : 0, nb = t + DB < kt1 ? b_bytes : 0;
+            char* nsa = a_stage(smem, r + DA);
+            char* nsb = b_stage(smem, r + DB);
+            const int nka = (t + DA) * BK, nkb = (t + DB) * BK;
 
-            const char* sa = st;
-            const char* sb = st + OA::BYTES;
             i32x4 fa[2][TM], fb[2][TN];
             auto read = [&](int g, int buf) {
 #pragma unroll
@@ -286,17 +320,23 @@ struct Dma16 {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 __builtin_amdgcn_sched_barrier(0);
-                // This k-group's share of the loads of tile t+STAGES-1 (into the
-                // stage tile t-1 used, which every wave has left at the barrier
-                // above), spread over the first NI k-groups: spread, so the loads
-                // do not leave in one burst after the barrier; within the first
-                // half of the tile, so that with two stages the last share still
-                // has half a tile to land (measured: 2-4 % faster than spreading
-                // over all).
+                // This k-group's share of the next loads (into the stages tile
+                // t-1 used, which every wave has left at the barrier above),
+                // spread over the first NI k-groups: spread, so the loads do
+                // not leave in one burst after the barrier; within the first
+                // half of the tile, so that with two stages the last share
+                // still has half a tile to land (measured: 2-4 % faster than
+                // spreading over all).  With unequal rings all of B goes
+                // before any of A (the order WAIT counts on).
                 constexpr int NI = NG < 2 ? NG : 2;
-                if (g < NI) {
-                    oa.issue(A, na, lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
-                    ob.issue(B, nb, ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI, (g + 1) * OB::IPW / NI);
+                if constexpr (DA == DB) {
+                    if (g < NI) {
+                        oa.issue(A, na, lda, m0, nka, nsa, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
+                        ob.issue(B, nb, ldb, n0, nkb, nsb, wave, g * OB::IPW / NI, (g + 1) * OB::IPW / NI);
+                    }
+                } else {
+                    if (g == 0) ob.issue(B, nb, ldb, n0, nkb, nsb, wave);
+                    if (g == NI - 1) oa.issue(A, na, lda, m0, nka, nsa, wave);
                 }
                 if (g + 1 < NG) read(g + 1, (g + 1) & 1);
 #pragma unroll
@@ -397,11 +437,12 @@ struct Dma16 {
 
 // EPI: as for gemm_kernel (a separate instantiation for 16-bit outputs that
 // run the elementwise epilogue).
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM, bool EPI>
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, bool AK, bool BKM, bool EPI,
+          int SBS = STAGES>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_dma_kernel(Params p)
 {
-    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM>;
+    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM, SBS>;
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
 
     select_batch(p);
@@ -426,7 +467,8 @@ gemm_dma_kernel(Params p)
     // own LDS base register instead of folding the fragment offsets into the
     // ds_read offsets -- 12 more instructions per k-tile, 2 % slower.  The
     // stream-K kernel, which needs arbitrary k-ranges, uses KT::mainloop.
-    constexpr int NG = KT::NG, KG = KT::KG, TM = KT::TM, TN = KT::TN, STAGE = KT::STAGE, LPT = KT::LPT;
+    constexpr int NG = KT::NG, KG = KT::KG, TM = KT::TM, TN = KT::TN;
+    constexpr int DA = KT::DA, DB = KT::DB, WAIT = KT::WAIT;
     constexpr int NT = KT::NT, WTM = KT::WTM, WTN = KT::WTN;
     using OA = typename KT::OA;
     using OB = typename KT::OB;
@@ -434,29 +476,36 @@ gemm_dma_kernel(Params p)
     const int nkt = (p.K + BK - 1) / BK;
     const int kvalid_last = p.K - (nkt - 1) * BK;
     const bool ragged = kvalid_last != BK;
+    if constexpr (DA == DB) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-        const bool live = s < nkt;
-        char* st = smem + s * STAGE;
-        oa.issue(p.A, live ? p.a_bytes : 0, p.lda, m0, s * BK, st, wave);
-        ob.issue(p.B, live ? p.b_bytes : 0, p.ldb, n0, s * BK, st + OA::BYTES, wave);
+        for (int s = 0; s < DA; ++s) {
+            const bool live = s < nkt;
+            oa.issue(p.A, live ? p.a_bytes : 0, p.lda, m0, s * BK, KT::a_stage(smem, s), wave);
+            ob.issue(p.B, live ? p.b_bytes : 0, p.ldb, n0, s * BK, KT::b_stage(smem, s), wave);
+        }
+    } else {
+        oa.issue(p.A, nkt > 0 ? p.a_bytes : 0, p.lda, m0, 0, KT::a_stage(smem, 0), wave);
+#pragma unroll
+        for (int s = 0; s < DB; ++s) {
+            ob.issue(p.B, s < nkt ? p.b_bytes : 0, p.ldb, n0, s * BK, KT::b_stage(smem, s), wave);
+            oa.issue(p.A, s + 1 < nkt ? p.a_bytes : 0, p.lda, m0, (s + 1) * BK, KT::a_stage(smem, s + 1), wave);
+        }
     }
     for (int t = 0; t < nkt; ++t) {
-        wait_vmcnt<LPT * (STAGES - 2)>();
-        char* st = smem + (t % STAGES) * STAGE;
+        wait_vmcnt<WAIT>();
+        char* sa = KT::a_stage(smem, t);
+        char* sb = KT::b_stage(smem, t);
         if (t == nkt - 1 && ragged && (AK || BKM)) {
             bare_barrier();
-            oa.template zero_tail<NT>(st, kvalid_last, tid);
-            ob.template zero_tail<NT>(st + OA::BYTES, kvalid_last, tid);
+            oa.template zero_tail<NT>(sa, kvalid_last, tid);
+            ob.template zero_tail<NT>(sb, kvalid_last, tid);
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
         }
         bare_barrier();
-        const bool more = t + STAGES - 1 < nkt;
-        const uint64_t na = more ? p.a_bytes : 0, nb = more ? p.b_bytes : 0;
-        char* nst = smem + ((t + STAGES - 1) % STAGES) * STAGE;
-        const int nk0 = (t + STAGES - 1) * BK;
-        const char* sa = st;
-        const char* sb = st + OA::BYTES;
+        const uint64_t na = t + DA < nkt ? p.a_bytes : 0, nb = t + DB < nkt ? p.b_bytes : 0;
+        char* nsa = KT::a_stage(smem, t + DA);
+        char* nsb = KT::b_stage(smem, t + DB);
+        const int nka = (t + DA) * BK, nkb = (t + DB) * BK;
         i32x4 fa[2][TM], fb[2][TN];
         auto read = [&](int g, int buf) {
 #pragma unroll
@@ -469,10 +518,14 @@ gemm_dma_kernel(Params p)
         for (int g = 0; g < NG; ++g) {
             __builtin_amdgcn_sched_barrier(0);
             constexpr int NI = NG < 2 ? NG : 2;
-            if (g < NI) {
-                oa.issue(p.A, na, p.lda, m0, nk0, nst, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
-                ob.issue(p.B, nb, p.ldb, n0, nk0, nst + OA::BYTES, wave, g * OB::IPW / NI,
-                         (g + 1) * OB::IPW / NI);
+            if constexpr (DA == DB) {
+                if (g < NI) {
+                    oa.issue(p.A, na, p.lda, m0, nka, nsa, wave, g * OA::IPW / NI, (g + 1) * OA::IPW / NI);
+                    ob.issue(p.B, nb, p.ldb, n0, nkb, nsb, wave, g * OB::IPW / NI, (g + 1) * OB::IPW / NI);
+                }
+            } else {
+                if (g == 0) ob.issue(p.B, nb, p.ldb, n0, nkb, nsb, wave);
+                if (g == NI - 1) oa.issue(p.A, na, p.lda, m0, nka, nsa, wave);
             }
             if (g + 1 < NG) read(g + 1, (g + 1) & 1);
 #pragma unroll
@@ -494,14 +547,14 @@ gemm_dma_kernel(Params p)
     KT::store_direct(p, m0, n0, acc, lane, wave);
 }
 
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES>
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, int SBS = STAGES>
 struct DmaInst {
     template <bool AK, bool BKM, bool EPI>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         Params copy = p;
         void* args[] = {&copy};
-        return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM, EPI>,
+        return hipLaunchKernel((const void*)&gemm_dma_kernel<TI, TO, BM, BN, BK, WM, WN, MI, STAGES, AK, BKM, EPI, SBS>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
     template <bool AK, bool BKM>
