@@ -84,6 +84,12 @@ _lib.gemm_load_tuning.argtypes = [ctypes.c_char_p]
 _lib.gemm_load_tuning.restype = _int
 _lib.gemm_tuning_size.argtypes = []
 _lib.gemm_tuning_size.restype = _int
+_lib.gemm_probe_mfma_flops.argtypes = [_int]
+_lib.gemm_probe_mfma_flops.restype = ctypes.c_double
+_lib.gemm_probe_mfma.argtypes = [_int, _int, _vp, _i64, _int, _vp, _vp]
+_lib.gemm_probe_mfma.restype = _int
+_lib.gemm_probe_hbm_read.argtypes = [_vp, _i64, _i64, _int, _vp, _vp]
+_lib.gemm_probe_hbm_read.restype = _int
 
 # gemm_dtype_t
 DTYPE_F32, DTYPE_F16_F32, DTYPE_BF16_BF16, DTYPE_F16_F16, DTYPE_BF16_F32 = range(5)
@@ -260,3 +266,23 @@ def gemm(a, b, c, stream=None, config=None):
 
 if not os.environ.get("MI355_GEMM_TUNING") and os.path.exists(DEFAULT_TABLE):
     gemm_load_tuning(DEFAULT_TABLE)
+
+
+# ---------------------------------------------------------------- measurement probes
+# (include/mi355_gemm_probe.h; not part of the GEMM path)
+
+PROBE_F16_16x16x32, PROBE_F16_32x32x16, PROBE_BF16_16x16x32 = range(3)
+
+
+def gemm_probe_mfma_flops(shape):
+    return _lib.gemm_probe_mfma_flops(shape)
+
+
+def gemm_probe_mfma(shape, rotate, operands, iters, grid, sink, stream=0):
+    """C ABI gemm_probe_mfma (device addresses). Returns the status."""
+    return _lib.gemm_probe_mfma(shape, int(bool(rotate)), operands, iters, grid, sink, stream)
+
+
+def gemm_probe_hbm_read(A, rows, row_bytes, seg_bytes, sink, stream=0):
+    """C ABI gemm_probe_hbm_read (device addresses). Returns the status."""
+    return _lib.gemm_probe_hbm_read(A, rows, row_bytes, seg_bytes, sink, stream)

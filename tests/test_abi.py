@@ -18,14 +18,18 @@ P = 1 << 20          # a fake, 16-byte aligned device address (never dereference
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    import glob
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gemm_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert "gemm_run" in names and len(names) >= 9
+    assert "gemm_run" in names and "gemm_probe_mfma" in names and len(names) >= 9
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -431,3 +435,21 @@ def test_noalloc_entry_point_host_checks():
     st = g.gemm_run_noalloc(M, N, K, "k", "k", "n", 0, big, 2 * big, 3 * big, K, K, N, 0, sk)
     assert st == b.GEMM_ERR_SCRATCH_LIMIT, g.gemm_status_str(st)
     assert "scratch" in g.gemm_status_str(st)
+
+
+def test_probe_entry_points_host_checks():
+    """The measurement probes validate their arguments before any HIP call."""
+    assert b.gemm_probe_mfma_flops(b.PROBE_F16_16x16x32) == 16 * 16 * 32 * 2
+    assert b.gemm_probe_mfma_flops(b.PROBE_F16_32x32x16) == 32 * 32 * 16 * 2
+    assert b.gemm_probe_mfma_flops(b.PROBE_BF16_16x16x32) == 16 * 16 * 32 * 2
+    assert b.gemm_probe_mfma_flops(3) == 0
+    assert b.gemm_probe_mfma(7, 1, P, 10, 256, 2 * P) == b.GEMM_ERR_BAD_SHAPE
+    assert b.gemm_probe_mfma(0, 1, P, -1, 256, 2 * P) == b.GEMM_ERR_BAD_SHAPE
+    assert b.gemm_probe_mfma(0, 1, P, 10, 0, 2 * P) == b.GEMM_ERR_BAD_SHAPE
+    assert b.gemm_probe_mfma(0, 1, NULL, 10, 256, 2 * P) == b.GEMM_ERR_NULL_PTR
+    assert b.gemm_probe_mfma(0, 1, P + 4, 10, 256, 2 * P) == b.GEMM_ERR_MISALIGNED
+    assert b.gemm_probe_hbm_read(P, 256, 8192, 96, 2 * P) == b.GEMM_ERR_BAD_SHAPE
+    assert b.gemm_probe_hbm_read(P, 255, 8192, 128, 2 * P) == b.GEMM_ERR_BAD_SHAPE
+    assert b.gemm_probe_hbm_read(P, 256, 8000, 128, 2 * P) == b.GEMM_ERR_BAD_LD
+    assert b.gemm_probe_hbm_read(NULL, 256, 8192, 128, 2 * P) == b.GEMM_ERR_NULL_PTR
+    assert b.gemm_probe_hbm_read(P + 8, 256, 8192, 128, 2 * P) == b.GEMM_ERR_MISALIGNED
