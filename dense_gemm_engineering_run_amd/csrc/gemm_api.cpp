@@ -311,23 +311,33 @@ bool is_scalar(int dtype, int config)
 // accepts (the first usable exact match, else the nearest usable entry within
 // a factor 2 overall), else the built-in heuristic.  The table is tuned on
 // single GEMMs, so a strided batch (batch > 1) goes to the heuristic.
+// Where the last choice of this thread came from (for MI355_GEMM_LOG).
+thread_local const char* t_source = "";
+
 template <class Usable>
 int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch, Usable usable)
 {
     std::call_once(g_env_once, load_env_table);
+    t_source = batch > 1 ? "heuristic, batched" : "heuristic";
     if (batch <= 1) {
         std::lock_guard<std::mutex> g(g_table_mu);
         const TuneEntry* best = nullptr;
         double best_d = 0;
         for (const TuneEntry& e : g_table) {
             if (e.dtype != dtype || e.a != a || e.b != b || e.c != c || !usable(e.config)) continue;
-            if (e.M == M && e.N == N && e.K == K) return e.config;
+            if (e.M == M && e.N == N && e.K == K) {
+                t_source = "table";
+                return e.config;
+            }
             double d = std::fabs(std::log2((double)std::max<int64_t>(M, 1) / std::max<int64_t>(e.M, 1))) +
                        std::fabs(std::log2((double)std::max<int64_t>(N, 1) / std::max<int64_t>(e.N, 1))) +
                        std::fabs(std::log2((double)std::max<int64_t>(K, 1) / std::max<int64_t>(e.K, 1)));
             if (!best || d < best_d) { best = &e; best_d = d; }
         }
-        if (best && best_d <= 1.0) return best->config;   // within a factor 2 overall
+        if (best && best_d <= 1.0) {   // within a factor 2 overall
+            t_source = "table, nearest shape";
+            return best->config;
+        }
     }
     // The kernel only sees the canonical (C n-major) problem: for C m-major
     // the operands and sizes swap.
@@ -400,7 +410,10 @@ bool epi_active(const gemm_epilogue_t* epi)
 int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K, int64_t batch,
                         uint64_t ws_bytes, bool vec16)
 {
-    if (!vec16) return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
+    if (!vec16) {
+        t_source = "heuristic, element-by-element loads";
+        return c == 'm' ? heuristic_scalar(dtype, N, M) : heuristic_scalar(dtype, M, N);
+    }
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
     const bool swap = c == 'm';
@@ -422,6 +435,7 @@ struct SelectMemo {
     uint64_t ws_bytes = 0;
     bool vec16 = false;
     int config = -1;
+    const char* source = "";
 };
 thread_local SelectMemo t_memo;
 
@@ -431,10 +445,12 @@ int select_for(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t 
     const unsigned gen = g_table_gen.load();
     SelectMemo& m = t_memo;
     if (m.valid && m.gen == gen && m.dtype == dtype && m.a == a && m.b == b && m.c == c && m.M == M &&
-        m.N == N && m.K == K && m.batch == batch && m.ws_bytes == ws_bytes && m.vec16 == vec16)
+        m.N == N && m.K == K && m.batch == batch && m.ws_bytes == ws_bytes && m.vec16 == vec16) {
+        t_source = m.source;
         return m.config;
+    }
     const int config = select_for_uncached(dtype, a, b, c, M, N, K, batch, ws_bytes, vec16);
-    m = SelectMemo{true, gen, dtype, a, b, c, M, N, K, batch, ws_bytes, vec16, config};
+    m = SelectMemo{true, gen, dtype, a, b, c, M, N, K, batch, ws_bytes, vec16, config, t_source};
     return config;
 }
 
@@ -501,6 +517,28 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     return GEMM_OK;
 }
 
+// MI355_GEMM_LOG=1 (read once): one line on stderr per GEMM call that gets
+// as far as choosing a config, naming the config, where the choice came from
+// and the launch status.
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char* v = std::getenv("MI355_GEMM_LOG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_call(const char* what, int dtype, int64_t M, int64_t N, int64_t K, char a, char b, char c, int64_t batch,
+              int config, const char* source, int status)
+{
+    int n = 0;
+    const mg::KernelEntry* all = entries(dtype, &n);
+    std::fprintf(stderr, "mi355_gemm: %s %s M=%lld N=%lld K=%lld a=%c b=%c c=%c batch=%lld -> %s [%s] %s\n", what,
+                 kDtypes[dtype].name, (long long)M, (long long)N, (long long)K, a, b, c, (long long)batch,
+                 config >= 0 && config < n ? all[config].name : "(none)", source, gemm_status_str(status));
+}
+
 int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
         const void* B, void* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream, int config,
         int64_t batch = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0, void* ws = nullptr,
@@ -525,10 +563,16 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
     x.sa = c == 'm' ? sb : sa;      // the C-m-major swap exchanges the operands
     x.sb = c == 'm' ? sa : sb;
     x.sc = sc;
-    if (config < 0) config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, vec16);
+    const char* source = "forced";
+    if (config < 0) {
+        config = select_for(dtype, a, b, c, M, N, K, batch, ws_bytes, vec16);
+        source = t_source;
+    }
     if (config < 0) return GEMM_ERR_NO_CONFIG;
     // bias follows the user's columns n: the canonical rows when C is m-major.
-    return launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
+    st = launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
+    if (log_enabled()) log_call("run", dtype, M, N, K, a, b, c, batch, config, source, st);
+    return st;
 }
 
 }  // namespace
@@ -685,7 +729,9 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, char a_major, char b_maj
     if ((a != 'k' && a != 'm') || (b != 'k' && b != 'n') || (c != 'n' && c != 'm'))
         return -GEMM_ERR_BAD_MAJOR;
     if (dtype < 0 || dtype >= GEMM_NUM_DTYPES) return -GEMM_ERR_BAD_DTYPE;
-    return select_for(dtype, a, b, c, M, N, K, 1, 0);
+    const int config = select_for(dtype, a, b, c, M, N, K, 1, 0);
+    if (log_enabled()) log_call("select", dtype, M, N, K, a, b, c, 1, config, t_source, GEMM_OK);
+    return config;
 }
 
 int gemm_last_config(void) { return t_last_config; }

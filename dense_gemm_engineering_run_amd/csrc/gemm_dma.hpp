@@ -25,8 +25,9 @@
 //  k-contiguous operand: [ROWS][BK]; 16 lanes reading one logical chunk of 16
 //    consecutive rows hit 16 distinct bank positions (as in gemm_kernel.hpp).
 //  m-contiguous operand: [BK][ROWS]; a transposing read touches 4 rows x 64 B
-//    per 32 lanes, so row k's chunks are XORed with 4 * (k mod 4) (rows sharing
-//    a window) to spread those 4 rows over the 16 chunk positions.
+//    (32x32x16 fragments) or 8 rows x 32 B (16x16x32) per 32 lanes, so row k's
+//    chunks are XORed with a key that spreads those rows over the 16 chunk
+//    positions (DmaOperand::mkey).
 //
 // K edge: rows k >= K of an m-contiguous operand lie outside its extent and
 // read as zeros.  For a k-contiguous operand the elements k >= K of the last,
@@ -62,7 +63,8 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // One operand's k-tile in the LDS ring, loaded with direct-to-LDS buffer loads.
-template <int ROWS, int BK, int NWAVES, bool KMAJ>
+// MI: the MFMA tile the fragments feed (it decides the m-contiguous swizzle).
+template <int ROWS, int BK, int NWAVES, bool KMAJ, int MI_ = 32>
 struct DmaOperand {
     static constexpr int ES = 2, CE = 8;
     static constexpr int BYTES = ROWS * BK * ES;
@@ -77,7 +79,20 @@ struct DmaOperand {
 
     int voff[IPW];
 
-    __device__ static __forceinline__ int mkey(int k) { return 4 * ((k / MRPW) % MXR); }
+    // Chunk XOR of row k of an m-contiguous tile.  A transposing read of a
+    // 32x32x16 fragment touches, per 32 lanes, 4 rows x 4 chunks (rows k0 ..
+    // k0+3): XOR with 4 (k mod 4) gives them 4 disjoint chunk groups.  A
+    // 16x16x32 fragment touches 8 rows x 2 chunks (rows k0 .. k0+3 and
+    // k0+8 .. k0+11): XOR with 2 ((k mod 4) + 4 ((k / 8) mod 2)) gives them
+    // 8 disjoint chunk pairs; the 32x32 key would put rows k and k+8 on the
+    // same banks (measured: SQ_LDS_BANK_CONFLICT at a quarter of the LDS
+    // cycles per such operand).  Rows narrower than the bank window keep the
+    // 32x32 key.
+    __device__ static __forceinline__ int mkey(int k)
+    {
+        if constexpr (MI_ == 16 && RCH >= 16) return 2 * ((k & 3) | ((k >> 1) & 4));
+        else return 4 * ((k / MRPW) % MXR);
+    }
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
     {
@@ -200,8 +215,8 @@ struct Dma16 {
     static constexpr int KG = MI == 32 ? 16 : 32;      // k per MFMA
     static constexpr int NG = BK / KG;                 // k-groups per tile
     static constexpr int R = MI == 32 ? 16 : 4;        // accumulators per MFMA tile and lane
-    using OA = DmaOperand<BM, BK, NW, AK>;
-    using OB = DmaOperand<BN, BK, NW, BKM>;
+    using OA = DmaOperand<BM, BK, NW, AK, MI>;
+    using OB = DmaOperand<BN, BK, NW, BKM, MI>;
     static constexpr int SA = STAGES, SB = SBS;        // ring depths
     static constexpr int DA = SA - 1, DB = SB - 1;     // k-tiles issued ahead
     static_assert(SA == SB || (SA == 3 && SB == 2), "A ring as deep as B's, or 3 A and 2 B stages");

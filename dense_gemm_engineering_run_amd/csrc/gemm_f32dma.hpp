@@ -358,7 +358,9 @@ struct F32Dma {
                                                                        (m * BN + n) * 4, 0, kDeviceCoherent);
                             } else if (m < p.M) {
                                 float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
-                                if (n + 3 < p.N) {
+                                // 128-bit stores only where C and ldc are 16-byte
+                                // aligned (never in the element-by-element configs).
+                                if (VEC && p.c_vec && n + 3 < p.N) {
                                     *(f32x4*)dst = o;
                                 } else {
 #pragma unroll

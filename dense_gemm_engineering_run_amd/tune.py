@@ -15,8 +15,10 @@ Each candidate is
      mistake this check rules out;
   2. checked on integer-valued inputs, whose exact result is unique: its
      output must equal, bit for bit, the output of the library's default
-     config for the same key (the default configs are the ones the test suite
-     checks against the CPU oracle);
+     config for the same key.  That reference output is itself checked first,
+     on 64 sampled rows (the first, the last and seeded ones, all columns),
+     against the exact product computed in fp64 on the host and rounded to
+     C's type; a key whose reference fails is not tuned;
   3. timed: `warmup` untimed runs, then `iters` runs each bracketed by HIP
      events on the launch stream; the median is the score.
 Every result is appended to a JSONL log as it is measured; a rerun skips the
@@ -151,6 +153,65 @@ def tune(keys, measure, config_names, log_path=None, table_path=None, verbose=Tr
     return best
 
 
+# ---------------------------------------------------------------- exact check of the reference
+
+def _logical(flat, dt_in, major_first, ld, rows, cols):
+    """fp64 logical rows x cols matrix from flat storage (float32, or fp16 /
+    bf16 bit patterns as uint16); major_first: the row index is contiguous."""
+    import numpy as np
+    flat = np.asarray(flat)
+    if dt_in == "f32":
+        v = flat.astype(np.float64)
+    elif dt_in == "f16":
+        v = flat.view(np.float16).astype(np.float64)
+    else:
+        v = (flat.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if major_first:
+        return v[: cols * ld].reshape(cols, ld)[:, :rows].T
+    return v[: rows * ld].reshape(rows, ld)[:, :cols]
+
+
+def _round_bits(x, dt_out):
+    """Bits of fp64 values (exact integers below 2^24) rounded to the output
+    type, to nearest even: uint32 for fp32, uint16 for fp16 / bf16."""
+    import numpy as np
+    if dt_out == "f32":
+        return x.astype(np.float32).view(np.uint32)
+    if dt_out == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)       # exact: |x| < 2^24
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def sample_rows(M, n=64, seed=0):
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(seed))
+    picks = set(range(min(16, M))) | set(range(max(0, M - 16), M))
+    picks |= set(int(r) for r in rng.integers(0, M, size=max(0, n - len(picks))))
+    return sorted(picks)
+
+
+def reference_rows_exact(key, A, B, lda, ldb, ldc, C, rows):
+    """True when rows `rows` of C (flat storage: float32, or uint16 bits for
+    16-bit outputs) equal the exact product of the integer-valued inputs,
+    rounded to C's type; else False and the first (row, column) that differs."""
+    import numpy as np
+    dt, a, b, c, M, N, K = key
+    din = {"f32": "f32", "f16_f32": "f16", "bf16_bf16": "bf16", "f16_f16": "f16", "bf16_f32": "bf16"}[DTYPE_NAMES[dt]]
+    dout = {"f32": "f32", "f16_f32": "f32", "bf16_bf16": "bf16", "f16_f16": "f16", "bf16_f32": "f32"}[DTYPE_NAMES[dt]]
+    Al = _logical(A, din, a == "m", lda, M, K)
+    Bl = _logical(B, din, b == "n", ldb, N, K)
+    want = _round_bits(Al[rows] @ Bl.T, dout)
+    flat = np.asarray(C)
+    bits = flat.view(np.uint32) if dout == "f32" else flat.view(np.uint16)
+    got = bits[: N * ldc].reshape(N, ldc)[:, :M].T[rows] if c == "m" else bits[: M * ldc].reshape(M, ldc)[rows, :N]
+    diff = np.argwhere(got != want)
+    if diff.size:
+        i, j = (int(v) for v in diff[0])
+        return False, (rows[i], j)
+    return True, None
+
+
 # ---------------------------------------------------------------- GPU measurement
 
 class GpuMeasure:
@@ -202,6 +263,10 @@ class GpuMeasure:
         if st != 0:
             raise RuntimeError(f"reference config failed: {g.gemm_status_str(st)}")
         torch.cuda.synchronize()
+        ok, where = reference_rows_exact(key, A, B, lda, ldb, ldc, (ref.view(torch.int32) if out_f32 else ref).cpu().numpy(),
+                                         sample_rows(M))
+        if not ok:
+            raise RuntimeError(f"reference config differs from the exact product at (row, column) {where}")
         self._ref = ref
         if self.timing_inputs is not None:
             TA, TB, tlda, tldb, _ = self.timing_inputs(key)

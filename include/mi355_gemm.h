@@ -53,6 +53,12 @@
  * Degenerate sizes.  M == 0 or N == 0: nothing is launched, GEMM_OK.
  * K == 0: C is filled with zeros (the empty sum); A and B are not read.
  *
+ * Logging.  With the environment variable MI355_GEMM_LOG set (to anything but
+ * 0) when the library first checks it, every GEMM call that chooses a config
+ * prints one line on stderr: the problem, the config, where the choice came
+ * from (forced, table, table nearest shape, heuristic) and the launch status;
+ * gemm_select_config prints its choice too.
+ *
  * Threads.  All functions are reentrant.  The only global state is the tuning
  * table, guarded by a mutex, a per-thread record of the last config, and the
  * device scratch array of gemm_run_noalloc (whose calls on one GPU must not

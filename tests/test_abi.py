@@ -4,6 +4,8 @@ selection and the tuning table are host logic and are covered here too."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -453,3 +455,26 @@ def test_probe_entry_points_host_checks():
     assert b.gemm_probe_hbm_read(P, 256, 8000, 128, 2 * P) == b.GEMM_ERR_BAD_LD
     assert b.gemm_probe_hbm_read(NULL, 256, 8192, 128, 2 * P) == b.GEMM_ERR_NULL_PTR
     assert b.gemm_probe_hbm_read(P + 8, 256, 8192, 128, 2 * P) == b.GEMM_ERR_MISALIGNED
+
+
+def test_log_env_prints_the_choice():
+    """MI355_GEMM_LOG=1: the config choice is printed with its source; a call
+    that fails validation prints nothing."""
+    code = (
+        "import dense_gemm_engineering_run_amd as g\n"
+        "g.gemm_load_tuning(None)\n"
+        f"assert g.gemm_run(-1, 8, 8, 'k', 'k', 'n', 0, {P}, {2 * P}, {3 * P}, 8, 8, 8, 0) != 0\n"
+        "print(g.gemm_select_config(4096, 4096, 4096, 'K', 'k', 'n', 1))\n")
+    env = dict(os.environ, MI355_GEMM_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("mi355_gemm:")]
+    assert len(lines) == 1, r.stderr
+    cfg = int(r.stdout.strip())
+    assert f"-> {g.gemm_config_describe(1, cfg)} [heuristic] ok" in lines[0], lines[0]
+    assert "select f16_f32 M=4096 N=4096 K=4096 a=k b=k c=n" in lines[0], lines[0]
+    env["MI355_GEMM_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                       timeout=120)
+    assert r.returncode == 0 and "mi355_gemm:" not in r.stderr

@@ -95,3 +95,38 @@ def test_stream_k_winner_gets_a_fallback_line(tmp_path):
         from dense_gemm_engineering_run_amd import _binding as b
         import os
         g.gemm_load_tuning(b.DEFAULT_TABLE if os.path.exists(b.DEFAULT_TABLE) else None)
+
+
+def test_reference_rows_exact_check_catches_planted_mistakes():
+    """The tuner's check of its reference output: the exact product, laid out
+    as C, passes for every dtype and C layout; a changed element, a C written
+    row-shifted and column-shifted each fail at the right place."""
+    import numpy as np
+
+    import gemm_inputs as gi
+    from dense_gemm_engineering_run_amd import tune as T
+    for dtype, lay in [("f32", "mnn"), ("f16_f32", "kkm"), ("bf16_bf16", "knn"), ("f16_f16", "mkm"),
+                       ("bf16_f32", "knm")]:
+        code = gi.DTYPE_CODE[dtype]
+        M, N, K = 70, 45, 300
+        p = gi.problem(M, N, K, lay[0], lay[1], lay[2], dtype, "int5", seed=3)
+        a_log, b_log = gi.draw_ab(M, N, K, "int5", seed=3)
+        exact = a_log.astype(np.float64) @ b_log.astype(np.float64).T
+        tout = gi.DTYPES[code][2]
+        cbits = T._round_bits(exact, tout)
+        flat = gi.store(cbits, lay[2] == "m", p["ldc"], fill=0)
+        key = (code, lay[0], lay[1], lay[2], M, N, K)
+        rows = T.sample_rows(M, n=20)
+        assert T.reference_rows_exact(key, p["A"], p["B"], p["lda"], p["ldb"], p["ldc"], flat, rows) == (True, None)
+        bad = flat.copy()
+        r, col = rows[5], 7
+        idx = (col * p["ldc"] + r) if lay[2] == "m" else (r * p["ldc"] + col)
+        bad[idx] ^= 1
+        assert T.reference_rows_exact(key, p["A"], p["B"], p["lda"], p["ldb"], p["ldc"], bad, rows) == (False, (r, col))
+        row_shift = gi.store(np.roll(cbits, 1, axis=0), lay[2] == "m", p["ldc"], fill=0)
+        assert not T.reference_rows_exact(key, p["A"], p["B"], p["lda"], p["ldb"], p["ldc"], row_shift, rows)[0]
+        shifted = gi.store(np.roll(cbits, 1, axis=1), lay[2] == "m", p["ldc"], fill=0)
+        assert not T.reference_rows_exact(key, p["A"], p["B"], p["lda"], p["ldb"], p["ldc"], shifted, rows)[0]
+    # row sample: first and last 16 rows, the rest seeded, sorted and unique
+    s = T.sample_rows(1000)
+    assert s == sorted(set(s)) and s[:16] == list(range(16)) and s[-16:] == list(range(984, 1000))
