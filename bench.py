@@ -4,10 +4,10 @@ One step = one GEMM C = A * B^T through the C ABI on inputs already resident
 in HBM.  The headline workload is the fp32 SGEMM M=N=K=8192 with A m-major,
 B n-major and C n-major (the size and layouts the CuTe DSL Ampere SGEMM
 example is run with in its docstring); the value is 2*M*N*K / t in TFLOP/s,
-timed with HIP events on the stream the kernels are launched on.  Every run
-is bracketed by events (the example's benchmark and the CuTe DSL benchmark
-notebook time each run the same way after warm-up runs); the mean and the
-median per launch are reported.
+timed with HIP events on the stream the kernels are launched on, after
+warm-up runs (the example's benchmark and the CuTe DSL benchmark notebook
+time runs the same way): the mean over a window of back-to-back launches,
+and the median of a second pass with an event after every launch.
 
 The JSON line also carries:
   roofline      achieved TFLOP/s of the GEMM kernel against the MI355X dense
@@ -345,12 +345,21 @@ class Problem:
                 n *= 2
 
     def time(self, iters):
-        """Per-launch times of `iters` back-to-back launches: an event is
-        recorded on the launch stream before the first launch and after each
-        one.  Returns the stats of the per-launch durations; mean_ms is the
-        whole window divided by iters."""
+        """Two passes of `iters` back-to-back launches on the launch stream:
+        the first bracketed by one pair of events (mean_ms: the window over
+        iters), the second with an event after every launch (the per-launch
+        median, min and max; for kernels of a few microseconds the events
+        between launches add their own time)."""
         import torch
         torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(iters):
+            self.launch()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        window = e0.elapsed_time(e1) / iters
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
         ev[0].record(self.stream)
         for i in range(iters):
@@ -358,7 +367,7 @@ class Problem:
             ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
         st = _stats([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
-        st["mean_ms"] = ev[0].elapsed_time(ev[iters]) / iters
+        st["mean_ms"] = window
         return st
 
     def time_sustained(self, min_s=0.1, per_launch_ms=None):
@@ -393,11 +402,12 @@ class Problem:
         while time.perf_counter() - t0 < min_warm_s:
             graph.replay()
             torch.cuda.synchronize()
+        rs = torch.cuda.current_stream()          # replay() launches on the current stream
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(s)
+        e0.record(rs)
         graph.replay()
-        e1.record(s)
+        e1.record(rs)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
