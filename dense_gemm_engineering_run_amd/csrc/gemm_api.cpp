@@ -251,7 +251,6 @@ void load_env_table()
 // Built-in choice when the table has nothing for this dtype and layout.
 int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_kmajor, int64_t batch)
 {
-    (void)K;
     auto pick = [&](const char* tile) {
         std::string name = std::string(kDtypes[dtype].name) + " " + tile;
         int id = find_config(dtype, name);
@@ -272,13 +271,19 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
         if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 dma");
         return pick("64x64x64 w2x2 mfma16 s2 swz");
     }
-    // The 256x256 tile on 16x16x32 MFMAs holds a higher clock under the
-    // power limit than on 32x32x16 ones and wins on one wave of tiles and for
-    // 16-bit outputs; with fp32 outputs on grids of several waves (8192^2,
-    // 16384^2) the 32x32x16 form stays 3-7 % ahead.
-    if (tiles256 >= 192)
+    // Large problems with k-contiguous B and K >= 1024 take the ping-pong
+    // schedule (4-13 % ahead of the one-group schedules at 4096^3, 8192^2 x
+    // 4096 and 2 x 4096^3 batched, every 16-bit dtype; level at K = 1024;
+    // 2-3 % behind at K = 256 and 512, where the k-loop is a few tiles
+    // long).  Otherwise the 256x256 tile on 16x16x32 MFMAs holds a higher
+    // clock under the power limit than on 32x32x16 ones and wins on one wave
+    // of tiles and for 16-bit outputs; with fp32 outputs on grids of several
+    // waves (8192^2, 16384^2) the 32x32x16 form stays 3-7 % ahead.
+    if (tiles256 >= 192) {
+        if (b_kmajor && K >= 1024) return pick("256x256x64 w4x2 mfma16 s3x2 pp");
         return pick(kDtypes[dtype].out_bytes == 4 && tiles256 >= 512 ? "256x256x64 w4x2 mfma32 s2 dma"
                                                                       : "256x256x64 w4x2 mfma16 s2 dma");
+    }
     // Mid-size: the 128x128 tile, on 16x16x32 MFMAs when both operands are
     // k-contiguous (5-10 % faster at 2048^2); with an m/n-contiguous operand
     // the 32x32x16 form's transposing LDS reads suit it better (up to 30 %).

@@ -142,7 +142,7 @@ struct DmaOperand {
 
     // MFMA fragment: rows rbase .. rbase+MI-1 of the tile, k-group starting at kb.
     template <int MI>
-    __device__ __forceinline__ i32x4 frag(const char* t, int rbase, int kb, int lane) const
+    __device__ static __forceinline__ i32x4 frag(const char* t, int rbase, int kb, int lane)
     {
         if constexpr (KMAJ) {
             const int row = rbase + lane % MI;
@@ -176,7 +176,7 @@ struct DmaOperand {
     // Zero the elements k >= kvalid of every row of a k-contiguous tile (the
     // partial last k-tile), working with all NT threads of the workgroup.
     template <int NT>
-    __device__ __forceinline__ void zero_tail(char* t, int kvalid, int tid) const
+    __device__ static __forceinline__ void zero_tail(char* t, int kvalid, int tid)
     {
         if constexpr (KMAJ) {
             const int c0 = kvalid / CE;
@@ -562,6 +562,172 @@ gemm_dma_kernel(Params p)
     KT::store_direct(p, m0, n0, acc, lane, wave);
 }
 
+// Ping-pong schedule of the 8-wave configs with k-contiguous B (two groups of
+// four waves; waves w and w + 4 share a SIMD).  Under the schedule of
+// gemm_dma_kernel the two waves of a SIMD take the MFMA pipe in turn, the
+// older first, so after each k-tile's barrier one of them soon waits at the
+// next barrier while the other runs the rest of its MFMAs alone between LDS
+// waits (measured with per-wave cycle counters at 4096^3: ~2800 cycles per
+// k-tile for 2048 cycles of MFMA work).  Here the groups trade roles in
+// phases one k-tile of MFMAs long: while group 0 multiplies tile t out of
+// registers, group 1 issues its loads and reads tile t's fragments; then
+// group 1 multiplies tile t while group 0 issues its loads and reads tile
+// t + 1.  A barrier closes each phase, so every SIMD always has one wave
+// whose operands are all in registers (~2340 cycles per k-tile).
+//
+// Loads: group 1 issues every A load (3-stage ring; tile t + 2 in phase A
+// of tile t), group 0 every B load (2-stage ring; tile t + 2 in phase B of
+// tile t).  Each goes into the slot of a tile that both groups have read
+// and waited for (lgkmcnt(0)) before the barrier that opens the phase.
+// Tile t + 1 is published by the barrier that closes phase A of tile t:
+// before it group 0 waits for all its loads (B of t + 1) and group 1 for
+// all but the last tile's (A of t + 2 may still be in flight).
+// The accumulation order of every C element is that of gemm_dma_kernel
+// (k-groups in order, tiles in order), so the two give identical bits.
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool EPI>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_pp_kernel(Params p)
+{
+    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, 3, AK, true, 2>;
+    static_assert(WM * WN == 8, "two groups of four waves");
+    constexpr int NG = KT::NG, KG = KT::KG, TM = KT::TM, TN = KT::TN, NT = KT::NT;
+    constexpr int WTM = KT::WTM, WTN = KT::WTN;
+    using LA = DmaOperand<BM, BK, 4, AK, MI>;     // loaded by group 1
+    using LB = DmaOperand<BN, BK, 4, true, MI>;   // loaded by group 0
+    constexpr int IA = LA::IPW, IB = LB::IPW;
+    static_assert(LA::BYTES == KT::OA::BYTES && LB::BYTES == KT::OB::BYTES, "same LDS tiles as Dma16");
+    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
+
+    select_batch(p);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, gw = wave & 3;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nkt = (p.K + BK - 1) / BK;
+    const int kvalid_last = p.K - (nkt - 1) * BK;
+    const bool zero_last = kvalid_last != BK;   // B is k-contiguous: the partial tile is zeroed past K
+
+    // A wave loads one operand only: one set of per-lane offsets (the
+    // operand's own layout) serves it, 8 registers fewer than two would take.
+    static_assert(IA == IB, "one offset set for either operand");
+    int voff[IA];
+    if (grp) {
+        LA o;
+        o.init(gw, lane, p.lda);
+#pragma unroll
+        for (int j = 0; j < IA; ++j) voff[j] = o.voff[j];
+    } else {
+        LB o;
+        o.init(gw, lane, p.ldb);
+#pragma unroll
+        for (int j = 0; j < IB; ++j) voff[j] = o.voff[j];
+    }
+    // Loads past the last tile get an empty extent (zeros into a free slot),
+    // so every phase has the same loads in flight.
+    auto issue_a = [&](int s) {
+        LA o;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) o.voff[j] = voff[j];
+        o.issue(p.A, s < nkt ? p.a_bytes : 0, p.lda, m0, s * BK, KT::a_stage(smem, s), gw);
+    };
+    auto issue_b = [&](int s) {
+        LB o;
+#pragma unroll
+        for (int j = 0; j < IB; ++j) o.voff[j] = voff[j];
+        o.issue(p.B, s < nkt ? p.b_bytes : 0, p.ldb, n0, s * BK, KT::b_stage(smem, s), gw);
+    };
+
+    typename KT::Acc acc;
+    KT::zero(acc);
+    i32x4 fa[NG][TM], fb[NG][TN];
+    auto read_all = [&](int s) {
+        const char* sa = KT::a_stage(smem, s);
+        const char* sb = KT::b_stage(smem, s);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[g][i] = LA::template frag<MI>(sa, wm * WTM + i * MI, g * KG, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[g][j] = LB::template frag<MI>(sb, wn * WTN + j * MI, g * KG, lane);
+        }
+    };
+    auto mfma_all = [&]() {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) mfma_step<TI, MI>(fa[g][i], fb[g][j], acc[i][j]);
+    };
+    // The partial last k-tile: zeros past K in both operands, by the whole
+    // workgroup, between the barrier that publishes the tile and any read.
+    auto zero_tail = [&](int s) {
+        LA::template zero_tail<NT>(KT::a_stage(smem, s), kvalid_last, tid);
+        LB::template zero_tail<NT>(KT::b_stage(smem, s), kvalid_last, tid);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are written
+        bare_barrier();
+    };
+
+    if (grp) {
+        issue_a(0);
+        issue_a(1);
+        wait_vmcnt<IA>();
+    } else {
+        issue_b(0);
+        issue_b(1);
+        wait_vmcnt<IB>();
+    }
+    bare_barrier();
+    if (nkt == 1 && zero_last) zero_tail(0);
+    if (!grp) {
+        read_all(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    }
+    // One loop per group, two barriers per k-tile in each (so they pair up);
+    // straight-line bodies keep fragments and accumulators in fixed registers.
+    if (!grp) {
+        for (int t = 0; t < nkt; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_all();                       // phase A: tile t
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<0>();                  // B of tile t + 1
+            bare_barrier();
+            if (t + 2 == nkt && zero_last) zero_tail(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_b(t + 2);                   // phase B: into tile t's B slot
+            if (t + 1 < nkt) read_all(t + 1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_sched_barrier(0);
+            bare_barrier();
+        }
+    } else {
+        for (int t = 0; t < nkt; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_a(t + 2);                   // phase A: into tile t-1's A slot
+            read_all(t);
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            wait_vmcnt<IA>();                 // A of tile t + 1
+            __builtin_amdgcn_sched_barrier(0);
+            bare_barrier();
+            if (t + 2 == nkt && zero_last) zero_tail(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_all();                       // phase B: tile t
+            __builtin_amdgcn_sched_barrier(0);
+            bare_barrier();
+        }
+    }
+    wait_vmcnt<0>();
+
+    if (TO == Out::F32 ? p.epi : EPI) {
+        KT::store_staged(p, smem, m0, n0, acc, tid, lane, wave);
+        return;
+    }
+    if constexpr (TO != Out::F32 && EPI) return;
+    KT::store_direct(p, m0, n0, acc, lane, wave);
+}
+
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, int SBS = STAGES>
 struct DmaInst {
     template <bool AK, bool BKM, bool EPI>
@@ -586,6 +752,37 @@ struct DmaInst {
         case 1: return go<true, false>(p, s);
         case 2: return go<false, true>(p, s);
         default: return go<false, false>(p, s);
+        }
+    }
+};
+
+// Launcher of the ping-pong configs: layouts with k-contiguous B run
+// gemm_pp_kernel; the others (B read with transposing loads, whose fragments
+// do not fit beside the accumulators without spills) run the 3 + 2-stage
+// gemm_dma_kernel.
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI>
+struct PpInst {
+    template <bool AK, bool EPI>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        Params copy = p;
+        void* args[] = {&copy};
+        return hipLaunchKernel((const void*)&gemm_pp_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, EPI>,
+                               dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
+    }
+    template <bool AK>
+    static hipError_t go(const Params& p, hipStream_t s)
+    {
+        if constexpr (TO != Out::F32)
+            if (p.epi) return go<AK, true>(p, s);
+        return go<AK, false>(p, s);
+    }
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        switch (layout) {
+        case 0: return go<true>(p, s);
+        case 2: return go<false>(p, s);
+        default: return DmaInst<TI, TO, BM, BN, BK, WM, WN, MI, 3, 2>::launch(layout, p, s);
         }
     }
 };

@@ -28,10 +28,16 @@ namespace mg {
      BM, BN, BK, WM, WN, MI, true,                                                  \
      &DmaInst<In::F16, Out::F16, BM, BN, BK, WM, WN, MI, SA, SB>::launch, SA, true},
 
+#define MG_PP_ENTRY(BM, BN, BK, WM, WN, MI)                                          \
+    {"f16_f16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s3x2 pp",                  \
+     BM, BN, BK, WM, WN, MI, true,                                                  \
+     &PpInst<In::F16, Out::F16, BM, BN, BK, WM, WN, MI>::launch, 3, true},
+
 static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)
                                            MG_DMA_SK_CONFIGS_16(MG_DMA_SK_ENTRY)
                                            MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)
-                                               MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)};
+                                               MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)
+                                                   MG_PP_CONFIGS_16(MG_PP_ENTRY)};
 
 const KernelEntry* entries_f16_f16(int* n)
 {

@@ -474,8 +474,9 @@ __device__ __forceinline__ void store4(const Params& p, int m, int n, f32x4 v)
 // coalesced vector stores instead of one store per accumulator, and one copy
 // of the epilogue code.  get(v) returns accumulator v (a constant index once
 // the loops are unrolled), pos(v, r, c) its tile-local row and column.  The
-// LDS (LDS_BYTES from smem) must be free: a barrier follows the main loop
-// here before anything is written.  ROLLED keeps the loop over bands rolled
+// LDS (LDS_BYTES from smem) is the kernel's operand ring; a barrier at entry
+// waits until no wave still reads it or has loads into it in flight.
+// ROLLED keeps the loop over bands rolled
 // (fewer registers live at once: the persistent stream-K kernels, whose loop
 // state stays live across the store, need that for 256x256 tiles).
 template <Out TO, int BM, int BN, int NT, int NV, int LDS_BYTES, bool ROLLED = false, class Get, class Pos>
@@ -486,6 +487,10 @@ __device__ __forceinline__ void store_tile_via_lds(const Params& p, char* smem, 
     constexpr int RB = FIT >= BM ? BM : FIT >= 128 ? 128 : FIT >= 64 ? 64 : FIT >= 32 ? 32 : FIT >= 16 ? 16 : 8;
     static_assert(FIT >= 8 && BM % RB == 0, "LDS too small for the staged epilogue");
     float* t = (float*)smem;
+    // Every wave's loads into the ring (the asynchronous direct-to-LDS ones
+    // included: the fence waits for this wave's vmcnt) and LDS reads of it are
+    // complete before any wave writes the staging bands over it.
+    __syncthreads();
     auto band = [&](int b0) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {

@@ -179,6 +179,50 @@ def test_every_config_nonintegers_multi_tile():
             assert ok, (g.gemm_config_describe(code, cfg), info)
 
 
+def _config_id(code, name):
+    import dense_gemm_engineering_run_amd as g
+    return next(i for i in range(g.gemm_num_configs(code)) if g.gemm_config_describe(code, i) == name)
+
+
+def test_ping_pong_matches_single_group_schedule():
+    """The ping-pong config accumulates every C element in the order of the
+    3 + 2-stage kernel of the same tile, so the two give identical bits: fp16
+    4096^3 on N(0,1) in all 8 layouts (those with n-contiguous B run that
+    kernel itself), each also checked against the oracle over the whole of
+    C; then ragged bf16 -> bf16 and fp16 -> fp32 shapes (a partial last
+    k-tile, 2-tile and 3-tile k ranges, partial edge tiles)."""
+    M = N = K = 4096
+    a_log, b_log = gi.draw_ab(M, N, K, "n01", seed=77)
+    a16, b16 = gi.cast(a_log, "f16"), gi.cast(b_log, "f16")
+    pp = _config_id(1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp")
+    one = _config_id(1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 dma")
+    ref = None
+    for am, bm, cm in LAYOUTS8:
+        log(f"ping-pong fp16 4096^3 {am}{bm}{cm}")
+        prob = dict(M=M, N=N, K=K, a_major=am, b_major=bm, c_major=cm, dtype=1, in_type="f16",
+                    out_type="f32", lda=4096, ldb=4096, ldc=4096, c_first=(cm == "m"),
+                    A=gi.store(a16, am == "m", 4096), B=gi.store(b16, bm == "n", 4096))
+        if ref is None:
+            ref = gu.reference(prob)
+        full_check(prob, exact=False, config=pp, ref=ref)
+        c_pp, _, st = gu.run(prob, config=pp)
+        assert st == 0
+        c_one, _, st = gu.run(prob, config=one)
+        assert st == 0
+        assert np.array_equal(c_pp.view(np.uint32), c_one.view(np.uint32)), (am, bm, cm)
+    for dtype, kind, code in (("bf16_bf16", "n002", 2), ("f16_f32", "n01", 1)):
+        pfx = dtype + " 256x256x64 w4x2 mfma16 s3x2 "
+        pp, one = _config_id(code, pfx + "pp"), _config_id(code, pfx + "dma")
+        for (m, n, k), (am, bm) in itertools.product([(1000, 1100, 1000), (520, 770, 100), (300, 260, 150)],
+                                                     [("k", "k"), ("m", "k"), ("m", "n")]):
+            log(f"ping-pong {dtype} {m}x{n}x{k} {am}{bm}n")
+            prob = gi.problem(m, n, k, am, bm, "n", dtype, kind, seed=m + k)
+            full_check(prob, exact=False, config=pp)
+            c_pp, _, _ = gu.run(prob, config=pp)
+            c_one, _, _ = gu.run(prob, config=one)
+            assert np.array_equal(c_pp.view(np.uint8), c_one.view(np.uint8)), (dtype, m, n, k, am, bm)
+
+
 # ---------------------------------------------------------------- canaries and edge semantics
 
 @pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
@@ -365,18 +409,19 @@ def test_batched_direct_to_lds_kernels(dtype, layout):
     cfg = batched_case(4096, 4096, 104, tuple(layout), dtype, "int5", 2)
     name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
     log(f"  config {name}")
-    assert name.endswith("dma"), name
+    assert name.endswith(("dma", "pp")), name
 
 
 def test_batched_selection_counts_every_entry():
     """A strided batch is one launch over all its entries' tiles: 64 x 512^3
     and 16 x 1024^3 (whose batch-1 table entry names a 64x64 tile) both go to
-    the 256x256 direct-to-LDS kernel (one wave of its tiles: the 16x16x32
-    form), and stay exact (every entry in full)."""
+    a 256x256 direct-to-LDS kernel (one wave of its tiles) -- the one-group
+    16x16x32 schedule at K = 512, the ping-pong one at K = 1024 -- and stay
+    exact (every entry in full)."""
     import dense_gemm_engineering_run_amd as g
-    for M, batch in ((512, 64), (1024, 16)):
-        cfg = batched_case(M, M, 512, ("k", "k", "n"), "f16_f32", "int5", batch)
-        assert g.gemm_config_describe(1, cfg) == "f16_f32 256x256x64 w4x2 mfma16 s2 dma", g.gemm_config_describe(1, cfg)
+    for M, batch, want in ((512, 64, "s2 dma"), (1024, 16, "s3x2 pp")):
+        cfg = batched_case(M, M, M, ("k", "k", "n"), "f16_f32", "int5", batch)
+        assert g.gemm_config_describe(1, cfg) == "f16_f32 256x256x64 w4x2 mfma16 " + want, g.gemm_config_describe(1, cfg)
     log("batched selection: 256x256 tile for 64 x 512^3 and 16 x 1024^3")
 
 
@@ -656,7 +701,7 @@ def test_epilogue_large_direct_kernels():
         cfg = epi_case(4096, 4096, 64, tuple(layout), dtype, "int5", 2.0, 1.0, g.GEMM_ACT_RELU)
         name = g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)
         log(f"  {dtype} {layout}: {name}")
-        assert name.endswith("dma"), name
+        assert name.endswith(("dma", "pp")), name
 
 
 # ---------------------------------------------------------------- operands not 16-byte aligned
