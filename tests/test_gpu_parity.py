@@ -506,6 +506,24 @@ def test_stream_k_ragged_workload(kind, exact):
         sk_case(4095, 2049, 1028, ("k", "k", "n"), cfg, kind, ldc=2052, ref=ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16"])
+def test_stream_k_thin_edge_tiles(dtype):
+    """A last tile row and column that are almost entirely outside C (4097 x
+    2049: one row and one column past a multiple of 128 and of 256), whose
+    tiles fall partly in the data-parallel part and partly in the split
+    stream-K share.  Every stream-K config, C n-major and m-major (the thin
+    edge then lies along the other canonical index), all of C against the
+    oracle, bit-exact on integer inputs."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    for cfg in _sk_configs(dtype):
+        name = g.gemm_config_describe(code, cfg)
+        for M, N, K, layout in [(4097, 2049, 200, ("k", "k", "n")), (2049, 4097, 136, ("m", "k", "m"))]:
+            log(f"stream-K thin edges {name} {M}x{N}x{K} {''.join(layout)}")
+            need, _ = sk_case(M, N, K, layout, cfg, "int5", dtype=dtype)
+            assert need > 0
+
+
 @pytest.mark.parametrize("dtype", SK_DTYPES)
 def test_stream_k_data_parallel_waves_plus_split_tail(dtype):
     """More than two waves of tiles, not whole waves: data-parallel tiles
