@@ -33,14 +33,15 @@ struct DtypeInfo {
     const char* name;
     int in_bytes, out_bytes;
     const mg::KernelEntry* (*entries)(int*);
+    hipError_t (*strip)(int, bool, const mg::Params&, hipStream_t);
 };
 
 const DtypeInfo kDtypes[GEMM_NUM_DTYPES] = {
-    {"f32", 4, 4, mg::entries_f32},
-    {"f16_f32", 2, 4, mg::entries_f16_f32},
-    {"bf16_bf16", 2, 2, mg::entries_bf16_bf16},
-    {"f16_f16", 2, 2, mg::entries_f16_f16},
-    {"bf16_f32", 2, 4, mg::entries_bf16_f32},
+    {"f32", 4, 4, mg::entries_f32, mg::strip_f32},
+    {"f16_f32", 2, 4, mg::entries_f16_f32, mg::strip_f16_f32},
+    {"bf16_bf16", 2, 2, mg::entries_bf16_bf16, mg::strip_bf16_bf16},
+    {"f16_f16", 2, 2, mg::entries_f16_f16, mg::strip_f16_f16},
+    {"bf16_f32", 2, 4, mg::entries_bf16_f32, mg::strip_bf16_f32},
 };
 
 const mg::KernelEntry* entries(int dtype, int* n)
@@ -356,6 +357,7 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
 }
 
 thread_local int t_last_config = -1;
+thread_local int t_strip_m = 0, t_strip_n = 0;   // the last launch's strips (rows, columns of C)
 
 // Stream-K schedule of a persistent config (mg::KernelEntry::sk_occ > 0).
 // The grid is a fixed 256 CUs x sk_occ workgroups: nothing in the kernel
@@ -472,15 +474,42 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     const int64_t a_span = ((x.a == 'k' ? e.BM : e.BK) * x.lda + std::max(e.BM, e.BK)) * es;
     const int64_t b_span = ((x.b == 'k' ? e.BN : e.BK) * x.ldb + std::max(e.BN, e.BK)) * es;
     if (a_span >= ((int64_t)1 << 31) || b_span >= ((int64_t)1 << 31)) return GEMM_ERR_BAD_SHAPE;
-    const int64_t tiles_m = (x.M + e.BM - 1) / e.BM, tiles_n = (x.N + e.BN - 1) / e.BN;
+    // A last column (row) of C at most kStripMax wide past a multiple of the
+    // tile goes to the strip kernel (gemm_strip.hpp); the tiled kernel runs
+    // the full tiles.  Not for stream-K configs (their split tail already
+    // shares such tiles out) nor for element-by-element ones.
+    // Only where that saves a round of tiles: the workgroups of one round are
+    // estimated from the config's LDS ring (256 CUs x how many rings fit in
+    // 160 KB), and a strip that leaves the count of rounds unchanged would
+    // only add its own time.
+    int64_t strip_m = 0, strip_n = 0;
+    if (e.sk_occ == 0 && !e.scalar && x.K > 0) {
+        const int64_t rm = x.M % e.BM, rn = x.N % e.BN;
+        const int64_t sm = rm > 0 && rm <= mg::kStripMax && x.M > e.BM ? rm : 0;
+        const int64_t sn = rn > 0 && rn <= mg::kStripMax && x.N > e.BN ? rn : 0;
+        const int64_t ring = (int64_t)(e.dma ? e.stages : 2) * (e.BM + e.BN) * e.BK * es;
+        const int64_t slots = 256 * std::max<int64_t>(1, std::min<int64_t>(8, (160 << 10) / ring));
+        auto rounds = [&](int64_t dm, int64_t dn) {
+            return ((x.M - dm + e.BM - 1) / e.BM * ((x.N - dn + e.BN - 1) / e.BN) * x.batch + slots - 1) / slots;
+        };
+        const int64_t r0 = rounds(0, 0), rn_only = rounds(0, sn), rm_only = rounds(sm, 0), both = rounds(sm, sn);
+        if (rn_only < r0 && rn_only <= rm_only) strip_n = sn;
+        else if (rm_only < r0) strip_m = sm;
+        if (both < std::min(rn_only, rm_only)) { strip_m = sm; strip_n = sn; }
+        if ((x.M - strip_m) / e.BM * ((x.N - strip_n) / e.BN) * x.batch < mg::kStripMinTiles) strip_m = strip_n = 0;
+    }
+    t_strip_m = (int)strip_m;
+    t_strip_n = (int)strip_n;
+    const int64_t tiles_m = (x.M - strip_m + e.BM - 1) / e.BM, tiles_n = (x.N - strip_n + e.BN - 1) / e.BN;
     if (tiles_m * tiles_n >= ((int64_t)1 << 31)) return GEMM_ERR_BAD_SHAPE;
 
     mg::Params p;
     p.A = (const char*)x.A;
     p.B = (const char*)x.B;
     p.C = (char*)C;
-    p.M = (int)x.M; p.N = (int)x.N; p.K = (int)x.K;
+    p.M = (int)(x.M - strip_m); p.N = (int)(x.N - strip_n); p.K = (int)x.K;
     p.tiles_m = (int)tiles_m; p.tiles_n = (int)tiles_n;
+    p.strip0 = 0;
     p.group_m = (int)std::min<int64_t>(8, tiles_m);
     p.lda = x.lda; p.ldb = x.ldb; p.ldc = x.ldc;
     p.a_bytes = x.K > 0 ? x.a_bytes : 0;
@@ -518,6 +547,19 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     const int layout = (x.a == 'k' ? 0 : 2) + (x.b == 'k' ? 0 : 1);
     hipError_t err = e.launch(layout, p, (hipStream_t)stream);
     if (err != hipSuccess) return GEMM_ERR_HIP;
+    if (strip_n) {               // C's last columns, all rows
+        mg::Params q = p;
+        q.M = (int)x.M;
+        q.N = (int)x.N;
+        q.strip0 = (int)(x.N - strip_n);
+        if (kDtypes[dtype].strip(layout, false, q, (hipStream_t)stream) != hipSuccess) return GEMM_ERR_HIP;
+    }
+    if (strip_m) {               // C's last rows, the columns the tiles cover
+        mg::Params q = p;
+        q.M = (int)x.M;
+        q.strip0 = (int)(x.M - strip_m);
+        if (kDtypes[dtype].strip(layout, true, q, (hipStream_t)stream) != hipSuccess) return GEMM_ERR_HIP;
+    }
     t_last_config = config;
     return GEMM_OK;
 }
@@ -539,9 +581,12 @@ void log_call(const char* what, int dtype, int64_t M, int64_t N, int64_t K, char
 {
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
-    std::fprintf(stderr, "mi355_gemm: %s %s M=%lld N=%lld K=%lld a=%c b=%c c=%c batch=%lld -> %s [%s] %s\n", what,
+    char strips[64] = "";
+    if (std::strcmp(what, "run") == 0 && (t_strip_m || t_strip_n))   // canonical (C n-major) rows / columns
+        std::snprintf(strips, sizeof strips, " + strip kernel (%d rows, %d columns)", t_strip_m, t_strip_n);
+    std::fprintf(stderr, "mi355_gemm: %s %s M=%lld N=%lld K=%lld a=%c b=%c c=%c batch=%lld -> %s%s [%s] %s\n", what,
                  kDtypes[dtype].name, (long long)M, (long long)N, (long long)K, a, b, c, (long long)batch,
-                 config >= 0 && config < n ? all[config].name : "(none)", source, gemm_status_str(status));
+                 config >= 0 && config < n ? all[config].name : "(none)", strips, source, gemm_status_str(status));
 }
 
 int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, const void* A,
@@ -550,6 +595,7 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
         size_t ws_bytes = 0, const gemm_epilogue_t* epi = nullptr)
 {
     t_last_config = -1;
+    t_strip_m = t_strip_n = 0;
     if (!ws) ws_bytes = 0;
     bool vec16 = true;
     int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes, epi,

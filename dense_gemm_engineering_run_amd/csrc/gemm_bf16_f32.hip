@@ -1,6 +1,7 @@
 // Kernel instantiations for dtype bf16_f32 (inputs BF16, output F32).
 #include "gemm_streamk.hpp"
 #include "configs.def"
+#include "gemm_strip.hpp"
 
 namespace mg {
 
@@ -38,6 +39,11 @@ static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16
                                            MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)
                                                MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)
                                                    MG_PP_CONFIGS_16(MG_PP_ENTRY)};
+
+hipError_t strip_bf16_f32(int layout, bool rows, const Params& p, hipStream_t s)
+{
+    return StripInst<In::BF16, Out::F32>::launch(layout, rows, p, s);
+}
 
 const KernelEntry* entries_bf16_f32(int* n)
 {

@@ -1,6 +1,7 @@
 // Kernel instantiations for dtype f16_f16 (inputs F16, output F16).
 #include "gemm_streamk.hpp"
 #include "configs.def"
+#include "gemm_strip.hpp"
 
 namespace mg {
 
@@ -38,6 +39,11 @@ static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16
                                            MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)
                                                MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)
                                                    MG_PP_CONFIGS_16(MG_PP_ENTRY)};
+
+hipError_t strip_f16_f16(int layout, bool rows, const Params& p, hipStream_t s)
+{
+    return StripInst<In::F16, Out::F16>::launch(layout, rows, p, s);
+}
 
 const KernelEntry* entries_f16_f16(int* n)
 {

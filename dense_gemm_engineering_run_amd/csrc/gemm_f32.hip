@@ -1,6 +1,7 @@
 // Kernel instantiations for dtype f32 (inputs F32, output F32).
 #include "gemm_f32dma.hpp"
 #include "configs.def"
+#include "gemm_strip.hpp"
 
 namespace mg {
 
@@ -30,6 +31,11 @@ static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIG
                                            MG_F32DMA_SK_CONFIGS(MG_F32DMA_SK_ENTRY)
                                            MG_F32DMA_SCALAR_CONFIGS(MG_F32DMA_SCALAR_ENTRY)
                                            MG_SCALAR_CONFIGS_F32(MG_SCALAR_ENTRY)};
+
+hipError_t strip_f32(int layout, bool rows, const Params& p, hipStream_t s)
+{
+    return StripInst<In::F32, Out::F32>::launch(layout, rows, p, s);
+}
 
 const KernelEntry* entries_f32(int* n)
 {

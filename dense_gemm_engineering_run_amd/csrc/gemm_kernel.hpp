@@ -94,6 +94,7 @@ struct Params {
     int bias_rows;
     int act;              // Act
     int c_vec;            // C and ldc allow 16-byte stores (else element stores only)
+    int strip0;           // strip kernel: first column (or row) of C that it computes
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -836,5 +837,18 @@ const KernelEntry* entries_f16_f32(int* n);
 const KernelEntry* entries_bf16_bf16(int* n);
 const KernelEntry* entries_f16_f16(int* n);
 const KernelEntry* entries_bf16_f32(int* n);
+// Widest last column (row) of C that the launch path gives to the strip
+// kernel instead of a column (row) of tiles, and the least number of full
+// tiles for which it does so (below that the extra launch costs more).
+constexpr int kStripMax = 4;
+constexpr int kStripMinTiles = 64;
+
+// The strip kernel of each dtype (gemm_strip.hpp): layout as for a
+// KernelEntry's launch; rows selects a strip of C's last rows.
+hipError_t strip_f32(int layout, bool rows, const Params& p, hipStream_t s);
+hipError_t strip_f16_f32(int layout, bool rows, const Params& p, hipStream_t s);
+hipError_t strip_bf16_bf16(int layout, bool rows, const Params& p, hipStream_t s);
+hipError_t strip_f16_f16(int layout, bool rows, const Params& p, hipStream_t s);
+hipError_t strip_bf16_f32(int layout, bool rows, const Params& p, hipStream_t s);
 
 }  // namespace mg

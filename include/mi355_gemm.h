@@ -55,9 +55,17 @@
  *
  * Logging.  With the environment variable MI355_GEMM_LOG set (to anything but
  * 0) when the library first checks it, every GEMM call that chooses a config
- * prints one line on stderr: the problem, the config, where the choice came
- * from (forced, table, table nearest shape, heuristic) and the launch status;
- * gemm_select_config prints its choice too.
+ * prints one line on stderr: the problem, the config (and, when the last
+ * rows or columns of C went to the strip kernel, how many), where the choice
+ * came from (forced, table, table nearest shape, heuristic) and the launch
+ * status; gemm_select_config prints its choice too.
+ *
+ * Thin edges.  When C's last 1-4 columns (or rows, of C as computed: C
+ * n-major, or its transpose for C m-major) lie past a multiple of the
+ * chosen tile and leaving them to a small strip kernel saves a round of
+ * tiles, the call launches the tiled kernel on the full tiles and the strip
+ * kernel after it, on the same stream (not for stream-K configs or the
+ * element-by-element ones).
  *
  * Threads.  All functions are reentrant.  The only global state is the tuning
  * table, guarded by a mutex, a per-thread record of the last config, and the

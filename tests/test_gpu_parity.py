@@ -166,6 +166,69 @@ def test_every_config_pipeline_depths(dtype):
     log(f"{dtype}: {count} pipeline-depth cases exact")
 
 
+STRIP_TILE = {"f32": "f32 128x128x32 w2x2 mfma32 s2 dma", "f16_f32": "f16_f32 128x128x64 w2x2 mfma16 s4 dma",
+              "bf16_bf16": "bf16_bf16 128x128x64 w2x2 mfma16 s4 dma", "f16_f16": "f16_f16 128x128x64 w2x2 mfma16 s4 dma",
+              "bf16_f32": "bf16_f32 128x128x64 w2x2 mfma16 s4 dma"}
+# Shapes whose last tile row and column (128x128 tiles) hold 1-4 rows and
+# columns of C, and where leaving them to the strip kernel saves a round of
+# tiles: 561 -> 512 tiles for the fp32 config (two rings per CU), 289 -> 256
+# for the 16-bit ones (one ring per CU).
+STRIP_SHAPES = {"f32": [(2049, 4099), (4098, 2050)], "16": [(2049, 2051), (2050, 2052)]}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16_f32", "bf16_bf16", "f16_f16", "bf16_f32"])
+def test_thin_edge_strips(dtype):
+    """C's last rows and columns, when 1-4 wide past a multiple of the tile,
+    go to the strip kernel and the rest to the tiled kernel: both strips and
+    their corner, one K chunk of the strip kernel and two (the second
+    partial), all 8 layouts, NaN in the ld padding; all of C against the
+    oracle, bit-exact on integer inputs; then 4095x2049x1028 (a column strip
+    only) on real-valued data within the tolerance."""
+    code = gi.DTYPE_CODE[dtype]
+    cfg = _config_id(code, STRIP_TILE[dtype])
+    k2 = 2200 if dtype == "f32" else 4200
+    shapes = STRIP_SHAPES["f32" if dtype == "f32" else "16"]
+    for (M, N), K in zip(shapes, (200, k2)):
+        for am, bm, cm in LAYOUTS8:
+            log(f"strips {dtype} {M}x{N}x{K} {am}{bm}{cm}")
+            prob = gi.problem(M, N, K, am, bm, cm, dtype, "int5", seed=M + K, pad_fill=float("nan"))
+            full_check(prob, exact=True, config=cfg)
+    kind = {"f32": "u11", "bf16_bf16": "n002", "bf16_f32": "n002"}.get(dtype, "n01")
+    ldc = 2052 if gi.DTYPES[code][2] == "f32" else 2056       # 16-byte rows of C
+    prob = gi.problem(4095, 2049, 1028, "k", "k", "n", dtype, kind, seed=4, ldc=ldc)
+    full_check(prob, exact=False, config=cfg)
+
+
+def test_thin_edge_strips_with_epilogue_and_batch():
+    """The strip kernel runs the same epilogue (alpha, beta, bias, relu; bias
+    along rows for C m-major) and serves every entry of a strided batch; the
+    call log names the strips."""
+    import subprocess
+    import dense_gemm_engineering_run_amd as g
+    for dtype in ("f32", "bf16_bf16"):
+        cfg = _config_id(gi.DTYPE_CODE[dtype], STRIP_TILE[dtype])
+        M, N = STRIP_SHAPES["f32" if dtype == "f32" else "16"][0]
+        for layout in [("k", "k", "n"), ("m", "n", "m")]:
+            epi_case(M, N, 136, layout, dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg)
+    batched_case(1026, 1027, 72, ("m", "n", "m"), "f32", "int5", 2)       # 64x64 tiles: 578 -> 512
+    batched_case(1026, 1027, 72, ("k", "k", "n"), "f16_f32", "int5", 4)   # 128x128 tiles: 324 -> 256
+    code = (
+        "import sys, torch; sys.path.insert(0, '.');"
+        "import dense_gemm_engineering_run_amd as g;"
+        "a = torch.zeros(4095 * 1028, device='cuda'); b = torch.zeros(2049 * 1028, device='cuda');"
+        "c = torch.zeros(4095 * 2052, device='cuda');"
+        f"cfg = [g.gemm_config_describe(0, i) for i in range(g.gemm_num_configs(0))].index('{STRIP_TILE['f32']}');"
+        "st = g.gemm_run_config(4095, 2049, 1028, 'k', 'k', 'n', 0, a.data_ptr(), b.data_ptr(), c.data_ptr(),"
+        " 1028, 1028, 2052, torch.cuda.current_stream().cuda_stream, cfg);"
+        "torch.cuda.synchronize(); assert st == 0, st")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, MI355_GEMM_LOG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "strip kernel (0 rows, 1 columns)" in r.stderr, r.stderr[-2000:]
+    log("strips with epilogue and batch: exact; log names the strip")
+
+
 def test_every_config_nonintegers_multi_tile():
     import dense_gemm_engineering_run_amd as g
     for dtype, kind in [("f32", "u11"), ("f16_f32", "n01"), ("bf16_bf16", "n002")]:
@@ -634,16 +697,18 @@ def test_epilogue_every_config_exact(dtype):
 def test_epilogue_stream_k_ragged():
     """The ragged fp32 workload with an epilogue: the 128x128 stream-K config
     runs 512 whole tiles through the staged epilogue and 32 split tiles
-    through the reduction's, bit-exact on integer inputs; with a workspace and
-    no forced config the table's stream-K choice is taken."""
+    through the reduction's; with no forced config the table's choice (the
+    128x128 tile with the strip kernel for the last column) is taken; both
+    bit-exact on integer inputs."""
     import dense_gemm_engineering_run_amd as g
     sk = next(i for i in range(g.gemm_num_configs(0))
               if g.gemm_config_describe(0, i) == "f32 128x128x32 w2x2 mfma32 s2 dma sk")
-    for config in (sk, None):
+    table = g.gemm_select_config(4095, 2049, 1028, "k", "k", "n", 0)
+    for config, want in ((sk, sk), (None, table)):
         used = epi_case(4095, 2049, 1028, ("k", "k", "n"), "f32", "int5", 2.0, -0.5, g.GEMM_ACT_RELU,
                         config=config, seed=21)
-        assert used == sk, g.gemm_config_describe(0, used)
-    log("ragged 4095x2049x1028 with epilogue on stream-K: exact")
+        assert used == want, g.gemm_config_describe(0, used)
+    log("ragged 4095x2049x1028 with epilogue, stream-K and the table's choice: exact")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16_bf16", "f16_f32"])

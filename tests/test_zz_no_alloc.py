@@ -57,10 +57,12 @@ def _check(prob, got_na, flat_na, got_ws):
 
 def test_noalloc_matches_workspace_entry_point_two_calls():
     import dense_gemm_engineering_run_amd as g
-    # 1: the ragged fp32 problem with the config the library chooses when
-    # 64 MiB of workspace is available (the tuned 128x128 stream-K tile).
-    log("noalloc 1: f32 4095x2049x1028 kkn, default config")
-    prob, na, flat, ws, name, need = _run_both(4095, 2049, 1028, ("k", "k", "n"), "f32", -1, seed=3, ldc=2052)
+    # 1: the ragged fp32 problem on the 128x128 stream-K config (its split
+    # tail's partial tiles and counters in the scratch array).
+    sk = next(i for i in range(g.gemm_num_configs(0))
+              if g.gemm_config_describe(0, i) == "f32 128x128x32 w2x2 mfma32 s2 dma sk")
+    log("noalloc 1: f32 4095x2049x1028 kkn, f32 128x128x32 w2x2 mfma32 s2 dma sk")
+    prob, na, flat, ws, name, need = _run_both(4095, 2049, 1028, ("k", "k", "n"), "f32", sk, seed=3, ldc=2052)
     log(f"  {name}, workspace {need} bytes")
     assert name.endswith(" sk") and 0 < need <= g.GEMM_NOALLOC_SCRATCH_BYTES
     _check(prob, na, flat, ws)
