@@ -70,6 +70,7 @@ struct Canon {
     uint64_t a_bytes, b_bytes;
     int64_t batch, sa, sb, sc;   // batch count and strides in elements
     bool vec16;                  // 16-byte loads allowed (else scalar configs only)
+    bool c_trans;                // C stored transposed (the swap below taken the other way)
 };
 
 // Bytes spanned by `outer` rows of `ld` elements whose last row holds
@@ -160,11 +161,15 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
 }
 
 // C m-major: C^T (N x M, n-major) = B * A^T.  Swap the operands and sizes.
+// trans: the other way round (swap for C n-major, not for C m-major), for a
+// kernel that then stores C transposed.
 Canon canonicalise(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype,
-                   const void* A, const void* B, int64_t lda, int64_t ldb, int64_t ldc, bool vec16 = true)
+                   const void* A, const void* B, int64_t lda, int64_t ldb, int64_t ldc, bool vec16 = true,
+                   bool trans = false)
 {
     Canon x;
-    if (c == 'm') {
+    x.c_trans = trans;
+    if ((c == 'm') != trans) {
         x.M = N; x.N = M; x.K = K;
         x.A = B; x.lda = ldb; x.a = b == 'k' ? 'k' : 'm';
         x.B = A; x.ldb = lda; x.b = a == 'k' ? 'k' : 'n';
@@ -272,8 +277,9 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
         if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 dma");
         return pick("64x64x64 w2x2 mfma16 s2 swz");
     }
-    // Large problems with k-contiguous B and K >= 1024 take the ping-pong
-    // schedule (4-13 % ahead of the one-group schedules at 4096^3, 8192^2 x
+    // Large problems with k-contiguous B (or k-contiguous A: the ping-pong
+    // config then stores C transposed, with the operands the other way round)
+    // and K >= 1024 take the ping-pong schedule (4-13 % ahead of the one-group schedules at 4096^3, 8192^2 x
     // 4096 and 2 x 4096^3 batched, every 16-bit dtype; level at K = 1024;
     // 2-3 % behind at K = 256 and 512, where the k-loop is a few tiles
     // long).  Otherwise the 256x256 tile on 16x16x32 MFMAs holds a higher
@@ -281,7 +287,7 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // of tiles and for 16-bit outputs; with fp32 outputs on grids of several
     // waves (8192^2, 16384^2) the 32x32x16 form stays 3-7 % ahead.
     if (tiles256 >= 192) {
-        if (b_kmajor && K >= 1024) return pick("256x256x64 w4x2 mfma16 s3x2 pp");
+        if ((a_kmajor || b_kmajor) && K >= 1024) return pick("256x256x64 w4x2 mfma16 s3x2 pp");
         return pick(kDtypes[dtype].out_bytes == 4 && tiles256 >= 512 ? "256x256x64 w4x2 mfma32 s2 dma"
                                                                       : "256x256x64 w4x2 mfma16 s2 dma");
     }
@@ -358,6 +364,7 @@ int select(int dtype, char a, char b, char c, int64_t M, int64_t N, int64_t K)
 
 thread_local int t_last_config = -1;
 thread_local int t_strip_m = 0, t_strip_n = 0;   // the last launch's strips (rows, columns of C)
+thread_local bool t_c_trans = false;             // the last launch stored C transposed
 
 // Stream-K schedule of a persistent config (mg::KernelEntry::sk_occ > 0).
 // The grid is a fixed 256 CUs x sk_occ workgroups: nothing in the kernel
@@ -500,6 +507,7 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     }
     t_strip_m = (int)strip_m;
     t_strip_n = (int)strip_n;
+    t_c_trans = x.c_trans;
     const int64_t tiles_m = (x.M - strip_m + e.BM - 1) / e.BM, tiles_n = (x.N - strip_n + e.BN - 1) / e.BN;
     if (tiles_m * tiles_n >= ((int64_t)1 << 31)) return GEMM_ERR_BAD_SHAPE;
 
@@ -510,6 +518,7 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     p.M = (int)(x.M - strip_m); p.N = (int)(x.N - strip_n); p.K = (int)x.K;
     p.tiles_m = (int)tiles_m; p.tiles_n = (int)tiles_n;
     p.strip0 = 0;
+    p.c_trans = x.c_trans;
     p.group_m = (int)std::min<int64_t>(8, tiles_m);
     p.lda = x.lda; p.ldb = x.ldb; p.ldc = x.ldc;
     p.a_bytes = x.K > 0 ? x.a_bytes : 0;
@@ -581,9 +590,12 @@ void log_call(const char* what, int dtype, int64_t M, int64_t N, int64_t K, char
 {
     int n = 0;
     const mg::KernelEntry* all = entries(dtype, &n);
-    char strips[64] = "";
-    if (std::strcmp(what, "run") == 0 && (t_strip_m || t_strip_n))   // canonical (C n-major) rows / columns
-        std::snprintf(strips, sizeof strips, " + strip kernel (%d rows, %d columns)", t_strip_m, t_strip_n);
+    char strips[96] = "";
+    if (std::strcmp(what, "run") == 0) {   // strips in canonical rows / columns (C n-major)
+        if (t_strip_m || t_strip_n)
+            std::snprintf(strips, sizeof strips, " + strip kernel (%d rows, %d columns)", t_strip_m, t_strip_n);
+        if (t_c_trans) std::strncat(strips, ", operands swapped, C stored transposed", sizeof strips - std::strlen(strips) - 1);
+    }
     std::fprintf(stderr, "mi355_gemm: %s %s M=%lld N=%lld K=%lld a=%c b=%c c=%c batch=%lld -> %s%s [%s] %s\n", what,
                  kDtypes[dtype].name, (long long)M, (long long)N, (long long)K, a, b, c, (long long)batch,
                  config >= 0 && config < n ? all[config].name : "(none)", strips, source, gemm_status_str(status));
@@ -596,6 +608,7 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
 {
     t_last_config = -1;
     t_strip_m = t_strip_n = 0;
+    t_c_trans = false;
     if (!ws) ws_bytes = 0;
     bool vec16 = true;
     int st = validate(M, N, K, a, b, c, dtype, A, B, C, lda, ldb, ldc, batch, sa, sb, sc, ws, ws_bytes, epi,
@@ -620,6 +633,21 @@ int run(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, cons
         source = t_source;
     }
     if (config < 0) return GEMM_ERR_NO_CONFIG;
+    // A config that can store C transposed takes the other operand order when
+    // that turns an n-contiguous B into a k-contiguous one (A k, B n becomes
+    // A m, B k); not with an epilogue (its staged store runs along n).
+    {
+        int n = 0;
+        const mg::KernelEntry* all = entries(dtype, &n);
+        if (all[config].c_trans && !epi_active(epi) && x.a == 'k' && x.b == 'n') {
+            const bool swap = c != 'm';
+            x = canonicalise(M, N, K, a, b, c, dtype, A, B, lda, ldb, ldc, vec16, true);
+            x.batch = batch;
+            x.sa = swap ? sb : sa;
+            x.sb = swap ? sa : sb;
+            x.sc = sc;
+        }
+    }
     // bias follows the user's columns n: the canonical rows when C is m-major.
     st = launch(x, dtype, C, config, stream, ws, ws_bytes, epi, c == 'm');
     if (log_enabled()) log_call("run", dtype, M, N, K, a, b, c, batch, config, source, st);

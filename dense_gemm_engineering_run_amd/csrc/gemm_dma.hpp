@@ -409,6 +409,44 @@ struct Dma16 {
         }
     }
 
+    // Direct stores of the accumulators with C transposed (element (m, n) at
+    // n * ldc + m, Params::c_trans): a lane's 4 accumulators of a 16x16x32
+    // tile are 4 consecutive m of one n, so they go out as one vector.
+    __device__ static __forceinline__ void store_direct_t(const Params& p, int m0, int n0, const Acc& acc,
+                                                          int lane, int wave)
+    {
+        static_assert(MI == 16, "transposed store of 16x16x32 tiles");
+        const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n0 + wn * WTN + j * MI + (lane % MI);
+                const int m = m0 + wm * WTM + i * MI + (lane / 16) * 4;
+                if (n >= p.N) continue;
+                const int64_t idx = (int64_t)n * p.ldc + m;
+                if (p.c_vec && m + 3 < p.M) {
+                    if constexpr (TO == Out::F32) {
+                        *(f32x4*)((float*)p.C + idx) = acc[i][j];
+                    } else {
+                        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                        uint16_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            h[e] = TO == Out::F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e])
+                                                  : __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][e]);
+                        *(u32x2*)((uint16_t*)p.C + idx) = u32x2{(unsigned)h[0] | ((unsigned)h[1] << 16),
+                                                                (unsigned)h[2] | ((unsigned)h[3] << 16)};
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (m + r < p.M) store_out<TO>(p.C, idx + r, acc[i][j][r]);
+                }
+            }
+        }
+    }
+
     // The fp32 partial tile, row-major with pitch BN, at p.C, with
     // device-scope stores (read back by a workgroup that may sit on another
     // XCD).  row() is linear in q apart from a per-lane part, so each element's
@@ -725,7 +763,8 @@ gemm_pp_kernel(Params p)
         return;
     }
     if constexpr (TO != Out::F32 && EPI) return;
-    KT::store_direct(p, m0, n0, acc, lane, wave);
+    if (p.c_trans) KT::store_direct_t(p, m0, n0, acc, lane, wave);
+    else KT::store_direct(p, m0, n0, acc, lane, wave);
 }
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, int SBS = STAGES>

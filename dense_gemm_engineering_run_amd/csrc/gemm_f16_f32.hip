@@ -32,7 +32,7 @@ namespace mg {
 #define MG_PP_ENTRY(BM, BN, BK, WM, WN, MI)                                          \
     {"f16_f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s3x2 pp",                  \
      BM, BN, BK, WM, WN, MI, true,                                                  \
-     &PpInst<In::F16, Out::F32, BM, BN, BK, WM, WN, MI>::launch, 3, true},
+     &PpInst<In::F16, Out::F32, BM, BN, BK, WM, WN, MI>::launch, 3, true, 0, false, true},
 
 static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)
                                            MG_DMA_SK_CONFIGS_16(MG_DMA_SK_ENTRY)

@@ -95,6 +95,7 @@ struct Params {
     int act;              // Act
     int c_vec;            // C and ldc allow 16-byte stores (else element stores only)
     int strip0;           // strip kernel: first column (or row) of C that it computes
+    int c_trans;          // C stored transposed: element (m, n) at n * ldc + m (no epilogue)
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -797,6 +798,7 @@ struct KernelEntry {
     bool dma;          // direct HBM -> LDS loads
     int sk_occ;        // stream-K: persistent workgroups per CU (0: one workgroup per tile)
     bool scalar;       // element-by-element loads: any leading dimension, element-aligned pointers
+    bool c_trans;      // can store C transposed (Params::c_trans)
 };
 
 // VEC = false: element-by-element operand loads, for operands that are not

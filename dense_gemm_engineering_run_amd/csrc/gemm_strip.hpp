@@ -147,7 +147,7 @@ gemm_strip_kernel(Params p)
     auto store = [&](int i, int j, float x) {
         const int m = ROWS ? s0 + j : i, n = ROWS ? i : s0 + j;
         if (p.epi) store_epi<TO>(p, m, n, x);
-        else store_out<TO>(p.C, (int64_t)m * p.ldc + n, x);
+        else store_out<TO>(p.C, p.c_trans ? (int64_t)n * p.ldc + m : (int64_t)m * p.ldc + n, x);
     };
     if constexpr (LK) {
         // The 16 lanes of a row are 16 consecutive lanes of one wave.

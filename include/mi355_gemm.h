@@ -56,7 +56,8 @@
  * Logging.  With the environment variable MI355_GEMM_LOG set (to anything but
  * 0) when the library first checks it, every GEMM call that chooses a config
  * prints one line on stderr: the problem, the config (and, when the last
- * rows or columns of C went to the strip kernel, how many), where the choice
+ * rows or columns of C went to the strip kernel, how many; and whether the
+ * operands were swapped and C stored transposed), where the choice
  * came from (forced, table, table nearest shape, heuristic) and the launch
  * status; gemm_select_config prints its choice too.
  *
@@ -66,6 +67,11 @@
  * tiles, the call launches the tiled kernel on the full tiles and the strip
  * kernel after it, on the same stream (not for stream-K configs or the
  * element-by-element ones).
+ *
+ * Transposed store.  Configs whose names end in " pp" store C transposed when
+ * that gives them a k-contiguous B: for A k-major and B n-major (C n-major),
+ * or A m-major and B k-major (C m-major), without an epilogue, they compute
+ * C^T = B A^T and write it transposed, which is C in the caller's layout.
  *
  * Threads.  All functions are reentrant.  The only global state is the tuning
  * table, guarded by a mutex, a per-thread record of the last config, and the

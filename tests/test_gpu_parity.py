@@ -229,6 +229,46 @@ def test_thin_edge_strips_with_epilogue_and_batch():
     log("strips with epilogue and batch: exact; log names the strip")
 
 
+def test_ping_pong_transposed_store():
+    """A k with B n (C n-major) and A m with B k (C m-major): the ping-pong
+    config swaps the operands and stores C transposed (the other two layouts
+    are controls).  All of C against the oracle, bit-exact on integer inputs,
+    NaN in the ld padding; thin edges (4097 x 4098: both strips, stored
+    transposed too) and ragged K; a strided batch, which the heuristic gives
+    the ping-pong config; an epilogue (the plain order); the call log."""
+    import subprocess
+    import dense_gemm_engineering_run_amd as g
+    for dtype in ("f16_f32", "bf16_bf16", "f16_f16"):
+        code = gi.DTYPE_CODE[dtype]
+        cfg = _config_id(code, dtype + " 256x256x64 w4x2 mfma16 s3x2 pp")
+        for layout in (("k", "n", "n"), ("m", "k", "m"), ("k", "n", "m"), ("m", "k", "n")):
+            for M, N, K in ((4097, 4098, 72), (1000, 700, 300)):
+                log(f"transposed store {dtype} {M}x{N}x{K} {''.join(layout)}")
+                prob = gi.problem(M, N, K, *layout, dtype, "int5", seed=M + K, pad_fill=float("nan"))
+                full_check(prob, exact=True, config=cfg)
+    used = batched_case(1024, 1024, 1024, ("k", "n", "n"), "f16_f32", "int5", 12)
+    assert g.gemm_config_describe(1, used).endswith(" pp"), g.gemm_config_describe(1, used)
+    cfg = _config_id(1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp")
+    epi_case(1000, 700, 300, ("k", "n", "n"), "f16_f32", "int5", 2.0, -0.5, g.GEMM_ACT_RELU, config=cfg)
+    code = (
+        "import sys, torch; sys.path.insert(0, '.');"
+        "import dense_gemm_engineering_run_amd as g;"
+        "a = torch.zeros(1024 * 1024, dtype=torch.float16, device='cuda');"
+        "b = torch.zeros(1024 * 1024, dtype=torch.float16, device='cuda');"
+        "c = torch.zeros(1024 * 1024, device='cuda');"
+        "cfg = [g.gemm_config_describe(1, i) for i in range(g.gemm_num_configs(1))].index("
+        "'f16_f32 256x256x64 w4x2 mfma16 s3x2 pp');"
+        "st = g.gemm_run_config(1024, 1024, 1024, 'k', 'n', 'n', 1, a.data_ptr(), b.data_ptr(), c.data_ptr(),"
+        " 1024, 1024, 1024, torch.cuda.current_stream().cuda_stream, cfg);"
+        "torch.cuda.synchronize(); assert st == 0, st")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, MI355_GEMM_LOG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "operands swapped, C stored transposed" in r.stderr, r.stderr[-2000:]
+    log("transposed store: exact on every layout; batch and epilogue exact; log names it")
+
+
 def test_every_config_nonintegers_multi_tile():
     import dense_gemm_engineering_run_amd as g
     for dtype, kind in [("f32", "u11"), ("f16_f32", "n01"), ("bf16_bf16", "n002")]:
