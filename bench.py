@@ -23,7 +23,8 @@ The JSON line also carries:
                 65536x256x4096 tall-skinny with its HBM GB/s, the fp16 -> fp16
                 K sweep at 8192^2), and the rows built on the plain GEMM:
                 stream-K, the fused epilogue, the strided-batched mode,
-                operands that are not 16-byte aligned.
+                operands that are not 16-byte aligned; and one GPU's share of
+                the fp32 cube and of the tall-skinny GEMM split over eight GPUs.
 
 Other modes:
   --mnk M,N,K [--a_major --b_major --c_major --dtype ...]
@@ -99,6 +100,14 @@ WORKLOADS["fp16_batched_64x512"] = (512, 512, 512, "k", "k", "n", "f16_f32", "n0
                                     "fp16 strided-batched GEMM, 64 x (512x512x512) -> fp32, A k, B k, C n")
 WORKLOADS["fp32_ragged_unaligned"] = WORKLOADS["fp32_ragged"][:8] + (2049,
     "fp32 ragged GEMM 4095x2049x1028 with lda = ldb = 1029, ldc = 2049 (not 16-byte multiples)",)
+# One GPU's share when the two largest problems are split over eight GPUs
+# without a reduction: the fp32 cube with C over a 4 x 2 grid of GPUs (rows
+# M/4, columns N/2, each GPU holding its own slices of A and B), the
+# tall-skinny GEMM split along M.
+WORKLOADS["fp32_8192_shard8"] = (2048, 4096, 8192, "m", "n", "n", "f32", "u11", None,
+    "fp32 SGEMM 2048x4096x8192 (one GPU's share of 8192^3 over a 4 x 2 GPU grid), A m, B n, C n, uniform(-1,1)")
+WORKLOADS["bf16_skinny_shard8"] = (8192, 256, 4096, "k", "k", "n", "bf16_bf16", "n002", None,
+    "bf16 GEMM 8192x256x4096 -> bf16 (one GPU's share of 65536x256x4096 split along M over 8 GPUs), A k, B k, C n, normal(0,0.02)")
 OPTIONS = {
     "fp32_ragged_streamk": {"config": "f32 128x128x32 w2x2 mfma32 s2 dma sk"},
     "fp32_8192_epilogue": {"epilogue": "bias_relu"},
@@ -108,6 +117,7 @@ OPTIONS = {
 }
 NEXT_ROWS = list(OPTIONS)
 SWEEP = [w for w in WORKLOADS if w.startswith("fp16_sweep")]
+SHARD = [w for w in WORKLOADS if w.endswith("_shard8")]
 
 HEADLINE = "fp32_8192"
 
@@ -614,8 +624,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--others", default="all",
                     help="comma list of extra workloads to time, 'all' (every other workload: the five "
-                         "workloads' others, the fp16 K sweep and the stream-K / epilogue / batched / "
-                         "unaligned rows), 'sweep' (the fp16 K sweep), 'next' (those four rows) or 'none'")
+                         "workloads' others, the fp16 K sweep, the stream-K / epilogue / batched / "
+                         "unaligned rows and the eight-GPU shard shapes), 'sweep' (the fp16 K sweep), "
+                         "'next' (those four rows), 'shard' (the shard shapes) or 'none'")
     ap.add_argument("--iterations", "--other-steps", dest="iterations", type=int, default=100,
                     help="timed launches of each other workload (and of --mnk)")
     ap.add_argument("--warmup_iterations", type=int, default=10)
@@ -742,6 +753,8 @@ def main():
         others = SWEEP
     elif args.others == "next":
         others = NEXT_ROWS
+    elif args.others == "shard":
+        others = SHARD
     else:
         others = [w for w in args.others.split(",") if w]
     if others:

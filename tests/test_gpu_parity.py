@@ -93,6 +93,26 @@ def test_w5_bf16_tall_skinny(kind, exact):
     log(f"  {info}")
 
 
+# One GPU's share of the two largest problems split over eight GPUs with no
+# reduction (the fp32 cube over a 4 x 2 grid of GPUs, the tall-skinny GEMM
+# along M): tile counts of a half and an eighth of the chip's CUs, where the
+# tuned configs differ from those of the whole problems.
+@pytest.mark.parametrize("kind,exact", [("u11", False), ("int5", True)])
+def test_shard_fp32_2048x4096x8192(kind, exact):
+    log(f"shard fp32 2048x4096x8192 mnn {kind}")
+    prob = gi.problem(2048, 4096, 8192, "m", "n", "n", "f32", kind)
+    info = full_check(prob, exact)
+    log(f"  {info}")
+
+
+@pytest.mark.parametrize("kind,exact", [("n002", False), ("int5", True)])
+def test_shard_bf16_8192x256x4096(kind, exact):
+    log(f"shard bf16 8192x256x4096 kkn {kind}")
+    prob = gi.problem(8192, 256, 4096, "k", "k", "n", "bf16_bf16", kind)
+    info = full_check(prob, exact)
+    log(f"  {info}")
+
+
 # ---------------------------------------------------------------- edges and configs
 
 EDGE = [1, 2, 3, 15, 16, 17, 31, 33, 63, 65, 127, 129, 255, 257]
