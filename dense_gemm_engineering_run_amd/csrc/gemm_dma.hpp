@@ -409,6 +409,79 @@ struct Dma16 {
         }
     }
 
+    // The plain store through LDS, each wave on its own.  In the accumulator
+    // layout a store instruction writes 16 (or 32) consecutive columns of 4
+    // rows: row pieces of 64 bytes for fp32 output, 32 for 16-bit.  Their
+    // cost follows their number, not the bytes (measured on 256 x 256 tiles,
+    // one per CU: ~11 µs for the 64 MB of fp32 of fp16 4096^3 and as long for
+    // the 33.5 MB of bf16 of 65536 x 256), so here each wave writes its WTM x
+    // WTN block of C, converted to TO, into its share of the (free) ring,
+    // row-major, and reads it back in 16-byte chunks, 16-32 lanes per row: row
+    // pieces of WTN * sizeof(TO) bytes.  Rows are padded so that the four (or
+    // two) row groups of an MFMA tile's accumulators fall on disjoint banks.
+    // Needs every wave's loads landed and its ring reads done (the caller's
+    // barrier) and C allowing 16-byte stores (p.c_vec).
+    static constexpr int OBY = TO == Out::F32 ? 4 : 2;                 // bytes per output element
+    static constexpr int SPITCH = WTN * OBY + (MI == 16 ? 16 : 32);     // staged row pitch
+    static constexpr int SHARE = SMEM / NW;                             // LDS bytes per wave
+    static constexpr int SCPR = WTN * OBY / 16;                         // 16-byte chunks per row
+    static_assert(SCPR <= 64 && 64 % SCPR == 0, "a read instruction covers whole rows");
+    static constexpr int rows_per_pass()
+    {
+        for (int d = WTM; d >= MI; d -= MI)
+            if (WTM % d == 0 && d * SPITCH <= SHARE) return d;
+        return 0;
+    }
+    static constexpr int RPP = rows_per_pass();
+    // Whether a share of the ring holds a pass of whole MFMA row blocks (else
+    // the kernels store directly).
+    static constexpr bool ROWS_OK = RPP >= MI && RPP % (64 / SCPR) == 0;
+
+    __device__ static __forceinline__ void store_rows(const Params& p, char* smem, int m0, int n0, const Acc& acc,
+                                                      int lane, int wave)
+    {
+        static_assert(ROWS_OK, "LDS share too small for the staged store");
+        const int wm = wave / WN, wn = wave % WN;
+        char* w = smem + wave * SHARE;
+        constexpr int EPC = 16 / OBY;            // elements per chunk
+        constexpr int RPI = 64 / SCPR;           // rows per read instruction
+        const int mb = m0 + wm * WTM, nb = n0 + wn * WTN;
+#pragma unroll
+        for (int pass = 0; pass < WTM / RPP; ++pass) {
+#pragma unroll
+            for (int i = pass * RPP / MI; i < (pass + 1) * RPP / MI; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < R; ++q) {
+                        const int r = row(0, i, q, lane) - pass * RPP, c = col(0, j, lane);
+                        char* d = w + r * SPITCH + c * OBY;
+                        const float v = acc[i][j][q];
+                        if constexpr (TO == Out::F32) *(float*)d = v;
+                        else if constexpr (TO == Out::F16) *(_Float16*)d = (_Float16)v;
+                        else *(uint16_t*)d = __builtin_bit_cast(uint16_t, (__bf16)v);
+                    }
+#pragma unroll
+            for (int r0 = 0; r0 < RPP; r0 += RPI) {
+                const int r = r0 + lane / SCPR, ch = lane % SCPR;
+                const i32x4 v = *(const i32x4*)(w + r * SPITCH + ch * 16);
+                const int m = mb + pass * RPP + r, n = nb + ch * EPC;
+                if (m >= p.M) continue;
+                char* dst = p.C + ((int64_t)m * p.ldc + n) * OBY;
+                if (n + EPC <= p.N) {
+                    *(i32x4*)dst = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e)
+                        if (n + e < p.N) {
+                            if constexpr (OBY == 4) ((int*)dst)[e] = v[e];
+                            else ((uint16_t*)dst)[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e % 2)));
+                        }
+                }
+            }
+        }
+    }
+
     // Direct stores of the accumulators with C transposed (element (m, n) at
     // n * ldc + m, Params::c_trans): a lane's 4 accumulators of a 16x16x32
     // tile are 4 consecutive m of one n, so they go out as one vector.
@@ -597,7 +670,12 @@ gemm_dma_kernel(Params p)
         return;
     }
     if constexpr (TO != Out::F32 && EPI) return;
-    KT::store_direct(p, m0, n0, acc, lane, wave);
+    if (KT::ROWS_OK && p.c_vec) {
+        bare_barrier();   // every wave's loads have landed (vmcnt above) and its ring reads are done
+        if constexpr (KT::ROWS_OK) KT::store_rows(p, smem, m0, n0, acc, lane, wave);
+    } else {
+        KT::store_direct(p, m0, n0, acc, lane, wave);
+    }
 }
 
 // Ping-pong schedule of the 8-wave configs with k-contiguous B (two groups of
@@ -763,8 +841,14 @@ gemm_pp_kernel(Params p)
         return;
     }
     if constexpr (TO != Out::F32 && EPI) return;
-    if (p.c_trans) KT::store_direct_t(p, m0, n0, acc, lane, wave);
-    else KT::store_direct(p, m0, n0, acc, lane, wave);
+    if (p.c_trans) {
+        KT::store_direct_t(p, m0, n0, acc, lane, wave);
+    } else if (KT::ROWS_OK && p.c_vec) {
+        bare_barrier();   // every wave's loads have landed (vmcnt above) and its ring reads are done
+        if constexpr (KT::ROWS_OK) KT::store_rows(p, smem, m0, n0, acc, lane, wave);
+    } else {
+        KT::store_direct(p, m0, n0, acc, lane, wave);
+    }
 }
 
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES, int SBS = STAGES>
