@@ -404,12 +404,25 @@ SkPlan sk_plan(const mg::KernelEntry& e, int64_t tiles, int64_t nkt)
     return s;
 }
 
+// k-ranges per tile of a split-k config (mg::KernelEntry::split_occ > 0):
+// as many as fill 256 CUs with split_occ workgroups each, at most 32 and at
+// least two k-tiles per range.
+int split_count(const mg::KernelEntry& e, int64_t tiles, int64_t nkt)
+{
+    const int64_t slots = (int64_t)kSkCUs * e.split_occ;
+    int64_t s = tiles > 0 ? slots / tiles : 1;
+    s = std::min<int64_t>(s, std::min<int64_t>(32, nkt / 2));
+    return (int)std::max<int64_t>(1, s);
+}
+
 // Workspace a config needs for the canonical problem x (0 when none).
 uint64_t workspace_need(const mg::KernelEntry& e, int64_t M, int64_t N, int64_t K)
 {
-    if (e.sk_occ == 0) return 0;
+    if (e.sk_occ == 0 && e.split_occ == 0) return 0;
     const int64_t tiles = ((M + e.BM - 1) / e.BM) * ((N + e.BN - 1) / e.BN);
-    return sk_plan(e, tiles, (K + e.BK - 1) / e.BK).bytes;
+    const int64_t nkt = (K + e.BK - 1) / e.BK;
+    if (e.split_occ > 0) return (uint64_t)tiles * split_count(e, tiles, nkt) * e.BM * e.BN * 4;
+    return sk_plan(e, tiles, nkt).bytes;
 }
 
 // True when the epilogue does something (else the plain store runs).
@@ -433,7 +446,8 @@ int select_for_uncached(int dtype, char a, char b, char c, int64_t M, int64_t N,
     const bool swap = c == 'm';
     auto usable = [&](int config) {
         const mg::KernelEntry& e = all[config];
-        return e.sk_occ == 0 || (batch == 1 && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
+        return (e.sk_occ == 0 && e.split_occ == 0) ||
+               (batch == 1 && workspace_need(e, swap ? N : M, swap ? M : N, K) <= ws_bytes);
     };
     return select(dtype, a, b, c, M, N, K, batch, usable);
 }
@@ -490,7 +504,7 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     // 160 KB), and a strip that leaves the count of rounds unchanged would
     // only add its own time.
     int64_t strip_m = 0, strip_n = 0;
-    if (e.sk_occ == 0 && !e.scalar && x.K > 0) {
+    if (e.sk_occ == 0 && e.split_occ == 0 && !e.scalar && x.K > 0) {
         const int64_t rm = x.M % e.BM, rn = x.N % e.BN;
         const int64_t sm = rm > 0 && rm <= mg::kStripMax && x.M > e.BM ? rm : 0;
         const int64_t sn = rn > 0 && rn <= mg::kStripMax && x.N > e.BN ? rn : 0;
@@ -531,6 +545,7 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
     p.sk_first = p.sk_wgs = p.sk_base = p.sk_rem = 0;
     p.sk_part = nullptr;
     p.sk_count = nullptr;
+    p.split = 1;
     p.epi = epi_active(epi);
     p.alpha = epi ? epi->alpha : 1.f;
     p.beta = epi ? epi->beta : 0.f;
@@ -552,6 +567,13 @@ int launch(const Canon& x, int dtype, void* C, int config, void* stream, void* w
             p.sk_count = (int*)ws;
             p.sk_part = (float*)((char*)ws + sp.count_bytes);
         }
+    }
+    if (e.split_occ > 0) {
+        if (x.batch != 1) return GEMM_ERR_NO_CONFIG;
+        const uint64_t need = workspace_need(e, x.M, x.N, x.K);
+        if (!ws || ws_bytes < need) return GEMM_ERR_WORKSPACE;
+        p.split = split_count(e, tiles_m * tiles_n, (x.K + e.BK - 1) / e.BK);
+        p.sk_part = (float*)ws;
     }
     const int layout = (x.a == 'k' ? 0 : 2) + (x.b == 'k' ? 0 : 1);
     hipError_t err = e.launch(layout, p, (hipStream_t)stream);
@@ -685,6 +707,8 @@ int plan_ws(int64_t M, int64_t N, int64_t K, char a, char b, char c, int dtype, 
         if (!sp.ok) return GEMM_ERR_BAD_SHAPE;
         *need = sp.bytes;
         *count_bytes = sp.count_bytes;
+    } else if (e.split_occ > 0) {
+        *need = workspace_need(e, swap ? N : M, swap ? M : N, K);   // partial tiles only, no counters
     }
     return GEMM_OK;
 }
@@ -772,7 +796,7 @@ const char* gemm_status_str(int status)
     case GEMM_ERR_NO_CONFIG: return "no such tile config for this dtype";
     case GEMM_ERR_HIP: return "HIP runtime error at launch";
     case GEMM_ERR_TUNING_FILE: return "tuning table missing or malformed";
-    case GEMM_ERR_WORKSPACE: return "stream-K config without a workspace of the size it needs";
+    case GEMM_ERR_WORKSPACE: return "stream-K or split-k config without a workspace of the size it needs";
     case GEMM_ERR_BAD_EPILOGUE: return "unknown epilogue activation";
     case GEMM_ERR_SCRATCH_LIMIT:
         return "the config needs more workspace than the allocation-free entry point's fixed scratch (64 MiB)";

@@ -34,11 +34,17 @@ namespace mg {
      BM, BN, BK, WM, WN, MI, true,                                                  \
      &PpInst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI>::launch, 3, true, 0, false, true},
 
+#define MG_DMA_SPLIT_ENTRY(BM, BN, BK, WM, WN, MI, SA, SB, OCC)                       \
+    {"bf16_bf16 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s" #SA "x" #SB " dma split",       \
+     BM, BN, BK, WM, WN, MI, true,                                                  \
+     &Dma16SplitInst<In::BF16, Out::BF16, BM, BN, BK, WM, WN, MI, SA, SB>::launch, SA, true, 0, false, false, OCC},
+
 static const KernelEntry kEntries[] = {MG_CONFIGS_16(MG_ENTRY) MG_DMA_CONFIGS_16(MG_DMA_ENTRY)
                                            MG_DMA_SK_CONFIGS_16(MG_DMA_SK_ENTRY)
                                            MG_SCALAR_CONFIGS_16(MG_SCALAR_ENTRY)
                                                MG_DMA2_CONFIGS_16(MG_DMA2_ENTRY)
-                                                   MG_PP_CONFIGS_16(MG_PP_ENTRY)};
+                                                   MG_PP_CONFIGS_16(MG_PP_ENTRY)
+                                                       MG_DMA_SPLIT_CONFIGS_16(MG_DMA_SPLIT_ENTRY)};
 
 hipError_t strip_bf16_bf16(int layout, bool rows, const Params& p, hipStream_t s)
 {

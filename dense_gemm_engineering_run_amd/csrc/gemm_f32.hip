@@ -27,10 +27,16 @@ namespace mg {
     {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma" #MI " s2 swz scalar",              \
      BM, BN, BK, WM, WN, MI, true, &Inst<In::F32, Out::F32, BM, BN, BK, WM, WN, MI, true, false>::launch, 2, false, 0, true},
 
+#define MG_F32DMA_SPLIT_ENTRY(BM, BN, BK, WM, WN, ST, OCC)                            \
+    {"f32 " #BM "x" #BN "x" #BK " w" #WM "x" #WN " mfma32 s" #ST " dma split",         \
+     BM, BN, BK, WM, WN, 32, true, &F32DmaSplitInst<Out::F32, BM, BN, BK, WM, WN, ST>::launch, ST, true, \
+     0, false, false, OCC},
+
 static const KernelEntry kEntries[] = {MG_CONFIGS_F32(MG_ENTRY) MG_F32DMA_CONFIGS(MG_F32DMA_ENTRY)
                                            MG_F32DMA_SK_CONFIGS(MG_F32DMA_SK_ENTRY)
                                            MG_F32DMA_SCALAR_CONFIGS(MG_F32DMA_SCALAR_ENTRY)
-                                           MG_SCALAR_CONFIGS_F32(MG_SCALAR_ENTRY)};
+                                           MG_SCALAR_CONFIGS_F32(MG_SCALAR_ENTRY)
+                                               MG_F32DMA_SPLIT_CONFIGS(MG_F32DMA_SPLIT_ENTRY)};
 
 hipError_t strip_f32(int layout, bool rows, const Params& p, hipStream_t s)
 {

@@ -456,4 +456,18 @@ struct F32DmaInst {
     }
 };
 
+// Launcher of the fp32 split-k configs (gemm_split_kernel, gemm_split_reduce).
+template <Out TO, int BM, int BN, int BK, int WM, int WN, int STAGES>
+struct F32DmaSplitInst {
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        switch (layout) {
+        case 0: return launch_split<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, true, true>>(p, s);
+        case 1: return launch_split<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, true, false>>(p, s);
+        case 2: return launch_split<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, false, true>>(p, s);
+        default: return launch_split<F32Dma<TO, BM, BN, BK, WM, WN, STAGES, false, false>>(p, s);
+        }
+    }
+};
+
 }  // namespace mg

@@ -96,6 +96,7 @@ struct Params {
     int c_vec;            // C and ldc allow 16-byte stores (else element stores only)
     int strip0;           // strip kernel: first column (or row) of C that it computes
     int c_trans;          // C stored transposed: element (m, n) at n * ldc + m (no epilogue)
+    int split;            // split-k configs: k-ranges per tile (partial tiles in sk_part)
 };
 
 // Point A, B, C at this workgroup's batch entry.
@@ -799,6 +800,7 @@ struct KernelEntry {
     int sk_occ;        // stream-K: persistent workgroups per CU (0: one workgroup per tile)
     bool scalar;       // element-by-element loads: any leading dimension, element-aligned pointers
     bool c_trans;      // can store C transposed (Params::c_trans)
+    int split_occ;     // split-k: workgroups per CU the k-ranges are counted for (0: not split-k)
 };
 
 // VEC = false: element-by-element operand loads, for operands that are not

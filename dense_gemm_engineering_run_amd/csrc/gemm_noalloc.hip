@@ -3,9 +3,9 @@
 // gemm_run_noalloc is gemm_run_ws with the workspace taken from a fixed
 // array in device memory that the library owns (`scratch`, kScratchBytes),
 // for callers that cannot allocate (code under HIP graph capture, serving
-// loops, harnesses that forbid hipMalloc).  The stream-K configs are the only
-// ones that use a workspace: their arrival counters and partial tiles live
-// in it.  Each GPU holds its own copy of the array, from the library's first
+// loops, harnesses that forbid hipMalloc).  The stream-K and split-k configs
+// are the only ones that use a workspace: the stream-K arrival counters and
+// partial tiles, the split-k partial tiles, live in it.  Each GPU holds its own copy of the array, from the library's first
 // use on that GPU until the process ends.
 //
 // In host code `scratch` names a host-side stand-in, not device memory; its
@@ -84,8 +84,8 @@ extern "C" int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, char a_major, c
     int words = (int)(count_bytes / 16);
     uint4* counters = (uint4*)ws;
     void* args[] = {&counters, &words};
-    if (hipLaunchKernel((const void*)&zero_words, dim3((words + 255) / 256), dim3(256), args, 0,
-                        (hipStream_t)stream) != hipSuccess)
+    if (words > 0 && hipLaunchKernel((const void*)&zero_words, dim3((words + 255) / 256), dim3(256), args, 0,
+                                     (hipStream_t)stream) != hipSuccess)
         return GEMM_ERR_HIP;
     return gemm_run_ws(M, N, K, a_major, b_major, c_major, dtype, A, B, C, lda, ldb, ldc, ws, kScratchBytes,
                        stream, config);

@@ -155,6 +155,92 @@ gemm_sk_kernel(Params p)
     }
 }
 
+// Split-k form of the direct-to-LDS kernels (configs named `… split`), for
+// problems with few tiles and a long K.  The k-tiles of every C tile are cut
+// into p.split contiguous ranges, one workgroup per (tile, range): grid.x
+// takes the tiles as the data-parallel kernels do, grid.y the ranges.  Each
+// workgroup writes its fp32 partial tile (row-major BM x BN) to workspace
+// slot tile * p.split + range; gemm_split_reduce, launched next on the same
+// stream, adds the partials of every element in range order and stores C
+// through the elementwise epilogue.  No workgroup waits for or reads another's
+// partial, and the reduction is spread over the whole chip -- in the stream-K
+// kernel the last contributor to arrive reads all of its tile's partials
+// alone, which sets its tail (about 18 µs for eight 256 KB partials).
+// Results are deterministic: the order of every sum is fixed by p.split.
+template <class KT>
+__global__ void __launch_bounds__(KT::NT)
+gemm_split_kernel(Params p)
+{
+    constexpr int BM = KT::TILE_M, BN = KT::TILE_N, BK = KT::TILE_K;
+    __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int nkt = (p.K + BK - 1) / BK, r = blockIdx.y;
+    const int kt0 = (int)((int64_t)r * nkt / p.split), kt1 = (int)((int64_t)(r + 1) * nkt / p.split);
+
+    typename KT::OA oa;
+    typename KT::OB ob;
+    oa.init(wave, lane, p.lda);
+    ob.init(wave, lane, p.ldb);
+    typename KT::Acc acc;
+    KT::zero(acc);
+    KT::mainloop(p, smem, oa, ob, tm * BM, tn * BN, kt0, kt1, acc, tid, lane, wave);
+    Params q = p;   // the partial tile, row-major BM x BN
+    q.C = (char*)p.sk_part + ((int64_t)(tm * p.tiles_n + tn) * p.split + r) * KT::PART_BYTES;
+    q.ldc = BN;
+    KT::template store<true>(q, 0, 0, acc, lane, wave);
+}
+
+// Thread q adds the p.split partials of 16-byte chunk q of the partial
+// tiles (tile q / (BM * BN / 4), chunks row-major within it) and stores the
+// four elements through the epilogue.
+template <Out TO, int BM, int BN>
+__global__ void __launch_bounds__(256)
+gemm_split_reduce(Params p)
+{
+    constexpr int CPT = BM * BN / 4;   // chunks per tile
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int t = (int)(q / CPT), c = (int)(q % CPT);
+    if (t >= p.tiles_m * p.tiles_n) return;
+    const int m = (t / p.tiles_n) * BM + c / (BN / 4), n = (t % p.tiles_n) * BN + (c % (BN / 4)) * 4;
+    if (m >= p.M || n >= p.N) return;
+    const f32x4* src = (const f32x4*)p.sk_part + (int64_t)t * p.split * CPT + c;
+    f32x4 sum = src[0];
+#pragma unroll 4
+    for (int r = 1; r < p.split; ++r) sum += src[(int64_t)r * CPT];
+    store4<TO>(p, m, n, sum);
+}
+
+template <class KT>
+hipError_t launch_split(const Params& p, hipStream_t s)
+{
+    Params copy = p;
+    void* args[] = {&copy};
+    const unsigned tiles = (unsigned)(p.tiles_m * p.tiles_n);
+    hipError_t e = hipLaunchKernel((const void*)&gemm_split_kernel<KT>, dim3(tiles, (unsigned)p.split),
+                                   dim3(KT::NT), args, 0, s);
+    if (e != hipSuccess) return e;
+    const int64_t chunks = (int64_t)tiles * (KT::TILE_M * KT::TILE_N / 4);
+    return hipLaunchKernel((const void*)&gemm_split_reduce<KT::OUT, KT::TILE_M, KT::TILE_N>,
+                           dim3((unsigned)((chunks + 255) / 256)), dim3(256), args, 0, s);
+}
+
+// Launcher of the 16-bit split-k configs (A ring of SA stages, B ring of SB).
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int SA, int SB>
+struct Dma16SplitInst {
+    static hipError_t launch(int layout, const Params& p, hipStream_t s)
+    {
+        switch (layout) {
+        case 0: return launch_split<Dma16<TI, TO, BM, BN, BK, WM, WN, MI, SA, true, true, SB>>(p, s);
+        case 1: return launch_split<Dma16<TI, TO, BM, BN, BK, WM, WN, MI, SA, true, false, SB>>(p, s);
+        case 2: return launch_split<Dma16<TI, TO, BM, BN, BK, WM, WN, MI, SA, false, true, SB>>(p, s);
+        default: return launch_split<Dma16<TI, TO, BM, BN, BK, WM, WN, MI, SA, false, false, SB>>(p, s);
+        }
+    }
+};
+
 // Launcher of the 16-bit stream-K configs (the fp32 ones launch through
 // F32DmaInst<..., true>).
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, int STAGES>

@@ -9,7 +9,7 @@ update_on_change, tune(), benchmark()); the candidates are this library's
 compiled tile configs rather than JIT parameters.
 
 Each candidate is
-  1. launched through gemm_run_config (gemm_run_ws with a workspace for stream-K configs) and must report that the config it ran
+  1. launched through gemm_run_config (gemm_run_ws with a workspace for stream-K and split-k configs) and must report that the config it ran
      is the one requested (gemm_last_config) -- the notebook's tune() example
      compiles a fixed copy width whatever candidate it is given, which is the
      mistake this check rules out;
@@ -63,8 +63,9 @@ def load_log(path):
 
 
 def needs_workspace(name):
-    """Stream-K configs (names ending in ' sk') run only with a workspace."""
-    return name.endswith(" sk")
+    """Stream-K and split-k configs (names ending in ' sk' or ' split') run
+    only with a workspace."""
+    return name.endswith(" sk") or name.endswith(" split")
 
 
 def best_per_key(records, plain=False):
@@ -284,7 +285,7 @@ class GpuMeasure:
         C.zero_()
         args = self._args(key, C) + (cid,)
         s = torch.cuda.current_stream()
-        # Stream-K configs run through gemm_run_ws with a zero-filled workspace.
+        # Stream-K and split-k configs run through gemm_run_ws with a zero-filled workspace.
         need = g.gemm_workspace_size(M, N, K, a, b, c, dt, cid)
         ws = torch.zeros(max(need, 16) // 4, dtype=torch.int32, device="cuda") if need else None
 

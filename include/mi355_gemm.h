@@ -65,8 +65,8 @@
  * n-major, or its transpose for C m-major) lie past a multiple of the
  * chosen tile and leaving them to a small strip kernel saves a round of
  * tiles, the call launches the tiled kernel on the full tiles and the strip
- * kernel after it, on the same stream (not for stream-K configs or the
- * element-by-element ones).
+ * kernel after it, on the same stream (not for stream-K, split-k or
+ * element-by-element configs).
  *
  * Transposed store.  Configs whose names end in " pp" store C transposed when
  * that gives them a k-contiguous B: for A k-major and B n-major (C n-major),
@@ -112,7 +112,7 @@ typedef enum {
     GEMM_ERR_HIP = 9,          /* the HIP runtime reported an error at launch            */
     GEMM_ERR_TUNING_FILE = 10, /* tuning table missing or malformed                      */
     GEMM_ERR_BAD_EPILOGUE = 11, /* unknown epilogue activation                              */
-    GEMM_ERR_WORKSPACE = 12,   /* stream-K config without a large enough workspace       */
+    GEMM_ERR_WORKSPACE = 12,   /* stream-K / split-k config without a large enough workspace */
     GEMM_ERR_SCRATCH_LIMIT = 13 /* gemm_run_noalloc: the forced config needs more workspace
                                    than the library's fixed scratch holds               */
 } gemm_status_t;
@@ -180,11 +180,15 @@ int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major
  * gemm_run with a caller-owned device workspace, which lets the stream-K
  * configs run (persistent workgroups that split the k-iterations of the last
  * waves of tiles between them, for grids that would leave CUs idle; after the
- * Gluon multi-CTA tutorial, "Persistent kernels").  config_id < 0 chooses as
- * gemm_run does, except that a stream-K config named by the tuning table is
- * used when workspace_bytes covers gemm_workspace_size() for it; config_id >=
- * 0 forces that config (GEMM_ERR_WORKSPACE if it is a stream-K config and the
- * workspace is NULL or smaller than it needs).
+ * Gluon multi-CTA tutorial, "Persistent kernels"), and the split-k configs
+ * (names ending in " split": every tile's k-tiles cut into ranges, one
+ * workgroup per tile and range writing a partial tile, then a second kernel
+ * on the same stream adding the partials in range order, for problems with
+ * few tiles and a long K).  config_id < 0 chooses as gemm_run does, except
+ * that a stream-K or split-k config named by the tuning table is used when
+ * workspace_bytes covers gemm_workspace_size() for it; config_id >= 0 forces
+ * that config (GEMM_ERR_WORKSPACE if it needs a workspace and the workspace
+ * is NULL or smaller than it needs).
  *
  * The workspace must be 16-byte aligned (else GEMM_ERR_MISALIGNED), must not
  * overlap A, B or C (GEMM_ERR_ALIAS), and must be zero-filled before its
@@ -193,7 +197,8 @@ int gemm_run_batched(int64_t M, int64_t N, int64_t K, char a_major, char b_major
  * calls that may run at the same time (e.g. on different streams) need
  * different workspaces.  NULL / 0 is allowed: then this is gemm_run_config
  * (or gemm_run for config_id < 0).  Results are deterministic for a given
- * config and shape.  No batched form: stream-K configs take batch == 1.
+ * config and shape.  No batched form: stream-K and split-k configs take
+ * batch == 1.
  */
 int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                 int dtype, const void* A, const void* B, void* C,
@@ -205,7 +210,8 @@ int gemm_run_ws(int64_t M, int64_t N, int64_t K, char a_major, char b_major, cha
  * gemm_run_ws's: bias not 4-byte aligned -> GEMM_ERR_MISALIGNED; bias
  * overlapping C -> GEMM_ERR_ALIAS; unknown activation -> GEMM_ERR_BAD_EPILOGUE.
  * Every config runs the epilogue; in a stream-K config it is applied once per
- * element, by the workgroup that completes the tile.
+ * element, by the workgroup that completes the tile, in a split-k config by
+ * the reduction kernel.
  */
 int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                 int dtype, const void* A, const void* B, void* C,
@@ -220,7 +226,7 @@ int gemm_run_ex(int64_t M, int64_t N, int64_t K, char a_major, char b_major, cha
  * runs on, held from the first call on that GPU until the process ends.
  * Nothing is allocated per call; the caller passes A, B, C and the stream as
  * for gemm_run_ws.  config_id < 0 chooses as gemm_run_ws does with a
- * workspace of that size (a stream-K config only when it fits); a forced
+ * workspace of that size (a stream-K or split-k config only when it fits); a forced
  * config that needs more returns GEMM_ERR_SCRATCH_LIMIT.  When the config is
  * a stream-K one, a small kernel on `stream` first zeroes the arrival
  * counters, then the GEMM runs.  The array is the GPU's (the stream's
@@ -239,8 +245,8 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, char a_major, char b_major
 /*
  * Bytes of workspace that gemm_run_ws needs for this problem with config
  * config_id (< 0: the config the tuning table or the heuristic names for it),
- * written to *bytes; 0 when the config needs none (not stream-K, or its grid
- * is whole waves).  Host only: no HIP call.  Returns GEMM_OK,
+ * written to *bytes; 0 when the config needs none (neither stream-K nor
+ * split-k, or a stream-K config whose grid is whole waves).  Host only: no HIP call.  Returns GEMM_OK,
  * GEMM_ERR_NULL_PTR (bytes NULL), GEMM_ERR_BAD_SHAPE, GEMM_ERR_BAD_MAJOR,
  * GEMM_ERR_BAD_DTYPE or GEMM_ERR_NO_CONFIG.
  */
@@ -251,8 +257,8 @@ int gemm_workspace_size(int64_t M, int64_t N, int64_t K, char a_major, char b_ma
  * Same as gemm_run but with an explicit tile config (0 <= config_id <
  * gemm_num_configs(dtype)).  Used by the offline tuner and by the tests that
  * cover every config; GEMM_ERR_NO_CONFIG when the id is out of range,
- * GEMM_ERR_WORKSPACE for a stream-K config that needs a workspace (use
- * gemm_run_ws).
+ * GEMM_ERR_WORKSPACE for a stream-K or split-k config that needs a workspace
+ * (use gemm_run_ws).
  */
 int gemm_run_config(int64_t M, int64_t N, int64_t K, char a_major, char b_major, char c_major,
                     int dtype, const void* A, const void* B, void* C,

@@ -684,6 +684,87 @@ def test_stream_k_whole_waves_and_k_zero_need_no_workspace():
     assert need == 0
 
 
+# ---------------------------------------------------------------- split-k configs
+
+def _split_configs(dtype="f32"):
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    return [i for i in range(g.gemm_num_configs(code)) if g.gemm_config_describe(code, i).endswith(" split")]
+
+
+SPLIT_LAYOUTS = [("k", "k", "n"), ("k", "n", "n"), ("m", "k", "n"), ("m", "n", "n"), ("m", "n", "m")]
+
+
+@pytest.mark.parametrize("dtype", SK_DTYPES)
+def test_split_k_every_config_every_layout(dtype):
+    """Few tiles and a long, ragged K: 600 x 520 x 4100 is 9 tiles of 256x256
+    (28 k-ranges each) or 25 of 128x128 (20 each), the last k-tile partial,
+    M and N ragged; five layouts, C m-major among them.  All of C against the
+    oracle, bit-exact on integer inputs, twice (deterministic)."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    ref = gu.reference(gi.problem(600, 520, 4100, "k", "k", "n", dtype, "int5", seed=5))
+    cfgs = _split_configs(dtype)
+    assert len(cfgs) == 2
+    for cfg in cfgs:
+        for layout in SPLIT_LAYOUTS:
+            log(f"split-k {g.gemm_config_describe(code, cfg)} {''.join(layout)} 600x520x4100")
+            need, _ = sk_case(600, 520, 4100, layout, cfg, "int5", dtype=dtype, ref=ref)
+            assert need > 0
+
+
+@pytest.mark.parametrize("dtype,kind", [("f32", "u11"), ("bf16_bf16", "n002"), ("f16_f32", "n01")])
+def test_split_k_float_inputs_and_short_k(dtype, kind):
+    """Real-valued inputs on the bf16 shard shape 8192 x 256 x 4096 (32 tiles
+    of 256x256 cut into 8 k-ranges; 128 of 128x128 into 4), within the
+    normwise tolerance; and K too short to split (one k-range: partial tiles
+    written and added back unchanged)."""
+    import dense_gemm_engineering_run_amd as g
+    code = gi.DTYPE_CODE[dtype]
+    ref = gu.reference(gi.problem(8192, 256, 4096, "k", "k", "n", dtype, kind, seed=5))
+    for cfg in _split_configs(dtype):
+        name = g.gemm_config_describe(code, cfg)
+        log(f"split-k {name} 8192x256x4096 {kind}")
+        need, info = sk_case(8192, 256, 4096, ("k", "k", "n"), cfg, kind, dtype=dtype, ref=ref)
+        log(f"  {info}")
+        assert need == 8192 * 256 * 4 * (8 if " 256x256x" in name else 4)
+        log(f"split-k {name} 300x200x40 int5")
+        sk_case(300, 200, 40, ("k", "n", "n"), cfg, "int5", dtype=dtype)
+
+
+def test_split_k_epilogue_and_no_alloc_entry_point():
+    """The epilogue applied by the reduction kernel (bias, ReLU, beta != 0,
+    against the oracle on exact sums), and the allocation-free entry point
+    running a split-k config bit-identical to gemm_run_ws."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    for dtype in ["f32", "bf16_bf16"]:
+        for cfg in _split_configs(dtype):
+            log(f"split-k epilogue {g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)}")
+            assert epi_case(600, 520, 1100, ("k", "n", "n"), dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU,
+                            config=cfg) == cfg
+    cfg = _split_configs("bf16_bf16")[0]
+    prob = gi.problem(1000, 300, 4100, "k", "k", "n", "bf16_bf16", "int5", seed=3)
+    need = g.gemm_workspace_size(1000, 300, 4100, "k", "k", "n", prob["dtype"], cfg)
+    assert 0 < need <= g.GEMM_NOALLOC_SCRATCH_BYTES
+    a, b = gu.to_device(prob["A"]), gu.to_device(prob["B"])
+    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    outs = []
+    for noalloc in (False, True):
+        c = gu.c_buffer(prob)
+        args = (1000, 300, 4100, "k", "k", "n", prob["dtype"], a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                prob["lda"], prob["ldb"], prob["ldc"])
+        if noalloc:
+            st = g.gemm_run_noalloc(*args, s.cuda_stream, cfg)
+        else:
+            st = g.gemm_run_ws(*args, ws.data_ptr(), need, s.cuda_stream, cfg)
+        assert st == 0, g.gemm_status_str(st)
+        s.synchronize()
+        outs.append(gu.host_c(c, prob)[1])
+    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8))
+
+
 # ---------------------------------------------------------------- elementwise epilogue
 
 def _c_storage(c_log_bits, prob):
