@@ -205,6 +205,52 @@ def test_stream_k_workspace_size_and_errors_without_gpu():
     assert g.gemm_last_config() == -1
 
 
+def test_split_k_workspace_size_and_errors_without_gpu():
+    """Split-k configs: k-ranges per tile S = floor(256 * workgroups per CU /
+    tiles), at most 32 and at most half the k-tiles (at least 1), and a
+    workspace of tiles * S partial fp32 tiles; without one, or with a batch,
+    a forced split-k config is refused before any HIP call."""
+    def cfg(dtype, name):
+        return next(i for i in range(g.gemm_num_configs(dtype)) if g.gemm_config_describe(dtype, i) == name)
+    big = cfg(2, "bf16_bf16 256x256x64 w4x2 mfma16 s3x2 dma split")
+    small = cfg(2, "bf16_bf16 128x128x64 w2x2 mfma32 s2x2 dma split")
+    f32 = cfg(0, "f32 128x128x32 w2x2 mfma32 s2 dma split")
+    ws = lambda c, M, N, K, dtype=2, cm="n": g.gemm_workspace_size(M, N, K, "k", "k", cm, dtype, c)
+    # 8192 x 256: 32 tiles of 256x256 -> S = 8; 128 tiles of 128x128 at two per CU -> S = 4
+    assert ws(big, 8192, 256, 4096) == 32 * 8 * 256 * 256 * 4
+    assert ws(small, 8192, 256, 4096) == 128 * 4 * 128 * 128 * 4
+    # 600 x 520: 9 tiles -> 28 ranges; 25 tiles -> 20 (K = 4100: 65 k-tiles)
+    assert ws(big, 600, 520, 4100) == 9 * 28 * 256 * 256 * 4
+    assert ws(small, 600, 520, 4100) == 25 * 20 * 128 * 128 * 4
+    # one tile: capped at 32 ranges; a short K: at most half its k-tiles
+    assert ws(big, 256, 256, 8192) == 32 * 256 * 256 * 4
+    assert ws(big, 256, 256, 320) == 2 * 256 * 256 * 4          # 5 k-tiles -> 2 ranges
+    assert ws(big, 256, 256, 64) == 256 * 256 * 4               # one k-tile, one range
+    # many tiles: one range each (still a partial tile per tile)
+    assert ws(big, 8192, 8192, 1024) == 1024 * 256 * 256 * 4
+    # fp32 (32-deep k-tiles) and the C-m-major swap
+    assert ws(f32, 1024, 1024, 4096, dtype=0) == 64 * 8 * 128 * 128 * 4
+    assert ws(f32, 1024, 2048, 4096, dtype=0, cm="m") == ws(f32, 2048, 1024, 4096, dtype=0)
+
+    # K = 4104 (65 k-tiles as for 4100; rows of 8208 bytes, 16-byte multiples)
+    def run(config, ws_ptr, nbytes):
+        return g.gemm_run_ws(600, 520, 4104, "k", "k", "n", 2, P, P + (1 << 26), 1 << 32, 4104, 4104,
+                             520, ws_ptr, nbytes, 0, config)
+    need = ws(small, 600, 520, 4104)
+    assert need == ws(small, 600, 520, 4100)
+    assert run(small, 0, 0) == b.GEMM_ERR_WORKSPACE
+    assert run(small, 1 << 34, need - 16) == b.GEMM_ERR_WORKSPACE
+    assert run(small, (1 << 34) + 8, need) == b.GEMM_ERR_MISALIGNED
+    assert g.gemm_run_config(600, 520, 4104, "k", "k", "n", 2, P, P + (1 << 26), 1 << 32, 4104, 4104,
+                             520, 0, small) == b.GEMM_ERR_WORKSPACE
+    assert g.gemm_last_config() == -1
+    # The allocation-free entry point refuses a split that outgrows its scratch.
+    st = g.gemm_run_noalloc(8192, 8192, 8192, "k", "k", "n", 2, 1 << 34, 1 << 35, 1 << 36, 8192, 8192,
+                            8192, 0, big)
+    assert ws(big, 8192, 8192, 8192) > b.GEMM_NOALLOC_SCRATCH_BYTES
+    assert st == b.GEMM_ERR_SCRATCH_LIMIT, g.gemm_status_str(st)
+
+
 def test_select_config_never_returns_stream_k(tmp_path):
     sk_name = "f32 256x256x32 w2x2 mfma32 s2 dma sk"
     t = tmp_path / "t.txt"
