@@ -743,6 +743,9 @@ def test_split_k_epilogue_and_no_alloc_entry_point():
             log(f"split-k epilogue {g.gemm_config_describe(gi.DTYPE_CODE[dtype], cfg)}")
             assert epi_case(600, 520, 1100, ("k", "n", "n"), dtype, "int5", 2.0, -0.5, g.GEMM_ACT_RELU,
                             config=cfg) == cfg
+            # C m-major: the swapped problem, the bias indexed by its rows
+            assert epi_case(520, 600, 1100, ("m", "k", "m"), dtype, "int5", 1.0, 1.0, g.GEMM_ACT_RELU,
+                            config=cfg) == cfg
     cfg = _split_configs("bf16_bf16")[0]
     prob = gi.problem(1000, 300, 4100, "k", "k", "n", "bf16_bf16", "int5", seed=3)
     need = g.gemm_workspace_size(1000, 300, 4100, "k", "k", "n", prob["dtype"], cfg)
