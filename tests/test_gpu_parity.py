@@ -1003,8 +1003,9 @@ def test_unaligned_aligned_pointers_odd_ld_only():
 
 def test_graph_capture_stream_k_and_epilogue():
     """gemm_run_ex on a stream-K config (workspace counters reset by the
-    kernel itself, no memset), on a plain config with an epilogue and on the
-    stream-K config with the epilogue, each captured once: every replay, with
+    kernel itself, no memset), on a plain config with an epilogue, on the
+    stream-K config with the epilogue, and on a split-k config (two kernels
+    per call) with and without it, each captured once: every replay, with
     eager work between replays, equals the oracle bit for bit."""
     import torch
 
@@ -1017,7 +1018,9 @@ def test_graph_capture_stream_k_and_epilogue():
     bias = torch.arange(520, dtype=torch.float32, device="cuda") - 260.0
     want_epi = oracle.epilogue_ref(ref, 2.0, 0.0, None, bias.cpu().numpy(), oracle.ACT_RELU)
     relu = g.Epilogue(2.0, 0.0, bias.data_ptr(), g.GEMM_ACT_RELU)
-    cases = [(sk, None, ref), (-1, relu, want_epi), (sk, relu, want_epi)]
+    split = [i for i in range(g.gemm_num_configs(0)) if g.gemm_config_describe(0, i).endswith(" split")][1]
+    cases = [(sk, None, ref), (-1, relu, want_epi), (sk, relu, want_epi), (split, None, ref),
+             (split, relu, want_epi)]
     for cfg, epi, want in cases:
         need = g.gemm_workspace_size(600, 520, 200, "k", "k", "n", 0, cfg)
         assert (need > 0) == (cfg >= 0)
@@ -1040,7 +1043,7 @@ def test_graph_capture_stream_k_and_epilogue():
             got, _ = gu.host_c(c, prob)
             ok, info = gu.check(got, want, prob, True)
             assert ok, (cfg, rep, info)
-        if need:
+        if cfg == sk:
             assert int(torch.count_nonzero(ws[:256 // 4])) == 0     # counters back at zero
 
 
