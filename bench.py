@@ -35,7 +35,7 @@ Other modes:
   --use_cold_l2 rotate through enough copies of each problem's buffers
                 (at least 512 MB) that the caches cannot hold them;
   --probe mfma|hbm|all
-                the ceilings the kernels are judged against: 16-bit MFMA-only
+                the ceilings the kernels are measured against: 16-bit MFMA-only
                 throughput on register operands (per shape, operands changing
                 every MFMA or one fixed pair), and HBM -> LDS read rates per
                 segment size (include/mi355_gemm_probe.h).

@@ -1,7 +1,7 @@
 // gemm_probe.hip -- measurement probes behind include/mi355_gemm_probe.h.
 //
 // Not part of the GEMM path: two small kernels that measure the ceilings the
-// GEMM kernels are judged against on this part.
+// GEMM kernels are measured against on this part.
 //
 //  * mfma_probe: nothing but MFMAs on operands held in registers.  Each wave
 //    keeps 8 A and 8 B operand sets and 8 independent accumulators; with
