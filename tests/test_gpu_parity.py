@@ -1113,6 +1113,75 @@ def test_max_batch_exact():
     _exact_case(16, 24, 8, ("k", "k", "n"), "f32", A, B, batch=65535)
 
 
+# (M, N, K, layout, dtype, which operand is the 2^20-row one).  Each long
+# operand takes 4.5 GiB and C over 4 GiB, so tile origins, the 32-bit
+# extents of the buffer loads and the C offsets all pass the 2^32-byte mark;
+# the short side is 4 past a multiple of 256 or 8 past one (ragged tiles).
+OVER_4GIB = [
+    (1 << 20, 1028, 2304, ("k", "k", "n"), "f16_f32", "A"),
+    (1032, 1 << 20, 2304, ("m", "n", "m"), "bf16_f32", "B"),
+    (1 << 20, 1028, 1152, ("k", "k", "n"), "f32", "A"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,layout,dtype,big", OVER_4GIB)
+def test_operands_and_c_over_4gib_exact(M, N, K, layout, dtype, big):
+    """The long operand's rows repeat a seeded 997-row integer pattern
+    (so an offset that wrapped at 2^32 would read another row phase, or
+    another k, than the one it should); every element of C is compared
+    with the fp64 product of the pattern, which is exact for these values."""
+    import torch
+    import dense_gemm_engineering_run_amd as g
+    a_m, b_m, c_m = layout
+    code = gi.DTYPE_CODE[dtype]
+    _, tin, tout = gi.DTYPES[code]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[tin]
+    P = 997
+    rng = np.random.Generator(np.random.PCG64(11))
+    long_rows = M if big == "A" else N
+    short_rows = N if big == "A" else M
+    pat = rng.integers(-2, 3, size=(P, K)).astype(np.float32)
+    short = rng.integers(-2, 3, size=(short_rows, K)).astype(np.float32)
+    # C restricted to the pattern: (short x P) products, then spread by row phase.
+    small = (short.astype(np.float64) @ pat.astype(np.float64).T).astype(np.float32)
+    log(f"over 4 GiB {dtype} {M}x{N}x{K} {a_m}{b_m}{c_m} long {big}")
+
+    phase = torch.arange(long_rows, device="cuda") % P
+    pat_d = torch.from_numpy(pat).cuda().to(tdt)
+    # The long operand, k-contiguous (rows x K) or not (K x rows).
+    long_kmaj = (a_m if big == "A" else b_m) == "k"
+    long_d = pat_d[phase] if long_kmaj else pat_d.t()[:, phase].contiguous()
+    del pat_d
+    short_kmaj = (b_m if big == "A" else a_m) == "k"
+    short_d = torch.from_numpy(short).cuda().to(tdt)
+    short_d = short_d if short_kmaj else short_d.t().contiguous()
+    a_d, b_d = (long_d, short_d) if big == "A" else (short_d, long_d)
+    assert long_d.numel() * long_d.element_size() > (1 << 32)
+    lda = a_d.shape[1]
+    ldb = b_d.shape[1]
+    ldc = N if c_m == "n" else M
+    outer = M if c_m == "n" else N
+    assert outer * ldc * 4 > (1 << 32)
+    c = torch.full((outer, ldc), float("nan"), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    st = g.gemm_run(M, N, K, a_m, b_m, c_m, code, a_d.data_ptr(), b_d.data_ptr(), c.data_ptr(),
+                    lda, ldb, ldc, s.cuda_stream)
+    assert st == 0, g.gemm_status_str(st)
+    s.synchronize()
+    log(f"  config {g.gemm_config_describe(code, g.gemm_last_config())}")
+    del a_d, b_d, long_d, short_d
+    # small[s, p] = C at (short row s, long row with phase p).
+    small_d = torch.from_numpy(small).cuda()
+    if big == "A":
+        want = small_d.t()[phase]            # (M x N): row i is small[:, i % P]
+        got = c if c_m == "n" else c.t()
+    else:
+        want = small_d[:, phase]             # (M x N): column j is small[:, j % P]
+        got = c if c_m == "n" else c.t()
+    bad = int((got != want).sum())
+    assert bad == 0, f"{bad} of {M * N} elements differ"
+
+
 # ---------------------------------------------------------------- seeded random sweep
 
 def test_random_shapes_configs_layouts_exact():
