@@ -680,8 +680,8 @@ gemm_dma_kernel(Params p)
     }
 }
 
-// Ping-pong schedule of the 8-wave configs with k-contiguous B (two groups of
-// four waves; waves w and w + 4 share a SIMD).  Under the schedule of
+// Ping-pong schedule of the 8-wave configs (two groups of four waves; waves
+// w and w + 4 share a SIMD).  Under the schedule of
 // gemm_dma_kernel the two waves of a SIMD take the MFMA pipe in turn, the
 // older first, so after each k-tile's barrier one of them soon waits at the
 // next barrier while the other runs the rest of its MFMAs alone between LDS
@@ -702,16 +702,16 @@ gemm_dma_kernel(Params p)
 // all but the last tile's (A of t + 2 may still be in flight).
 // The accumulation order of every C element is that of gemm_dma_kernel
 // (k-groups in order, tiles in order), so the two give identical bits.
-template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool EPI>
+template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI, bool AK, bool BKM, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_pp_kernel(Params p)
 {
-    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, 3, AK, true, 2>;
+    using KT = Dma16<TI, TO, BM, BN, BK, WM, WN, MI, 3, AK, BKM, 2>;
     static_assert(WM * WN == 8, "two groups of four waves");
     constexpr int NG = KT::NG, KG = KT::KG, TM = KT::TM, TN = KT::TN, NT = KT::NT;
     constexpr int WTM = KT::WTM, WTN = KT::WTN;
     using LA = DmaOperand<BM, BK, 4, AK, MI>;     // loaded by group 1
-    using LB = DmaOperand<BN, BK, 4, true, MI>;   // loaded by group 0
+    using LB = DmaOperand<BN, BK, 4, BKM, MI>;    // loaded by group 0
     constexpr int IA = LA::IPW, IB = LB::IPW;
     static_assert(LA::BYTES == KT::OA::BYTES && LB::BYTES == KT::OB::BYTES, "same LDS tiles as Dma16");
     __shared__ __attribute__((aligned(1024))) char smem[KT::SMEM];
@@ -725,7 +725,9 @@ gemm_pp_kernel(Params p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int nkt = (p.K + BK - 1) / BK;
     const int kvalid_last = p.K - (nkt - 1) * BK;
-    const bool zero_last = kvalid_last != BK;   // B is k-contiguous: the partial tile is zeroed past K
+    // A k-contiguous operand's partial last tile is zeroed past K (an
+    // m-contiguous one reads zeros there: those rows lie past its extent).
+    const bool zero_last = (AK || BKM) && kvalid_last != BK;
 
     // A wave loads one operand only: one set of per-lane offsets (the
     // operand's own layout) serves it, 8 registers fewer than two would take.
@@ -881,32 +883,35 @@ struct DmaInst {
     }
 };
 
-// Launcher of the ping-pong configs: layouts with k-contiguous B run
-// gemm_pp_kernel; the others (B read with transposing loads, whose fragments
-// do not fit beside the accumulators without spills) run the 3 + 2-stage
+// Launcher of the ping-pong configs: A k with B k, A m with B k and A m with
+// B n run gemm_pp_kernel (the last with both operands read by transposing
+// loads: 254 VGPRs, no spills).  A k with B n reaches this launcher only with
+// an epilogue (without one the operands are swapped and C stored
+// transposed, which gives A m with B k) and runs the 3 + 2-stage
 // gemm_dma_kernel.
 template <In TI, Out TO, int BM, int BN, int BK, int WM, int WN, int MI>
 struct PpInst {
-    template <bool AK, bool EPI>
+    template <bool AK, bool BKM, bool EPI>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         Params copy = p;
         void* args[] = {&copy};
-        return hipLaunchKernel((const void*)&gemm_pp_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, EPI>,
+        return hipLaunchKernel((const void*)&gemm_pp_kernel<TI, TO, BM, BN, BK, WM, WN, MI, AK, BKM, EPI>,
                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.batch), dim3(WM * WN * 64), args, 0, s);
     }
-    template <bool AK>
+    template <bool AK, bool BKM>
     static hipError_t go(const Params& p, hipStream_t s)
     {
         if constexpr (TO != Out::F32)
-            if (p.epi) return go<AK, true>(p, s);
-        return go<AK, false>(p, s);
+            if (p.epi) return go<AK, BKM, true>(p, s);
+        return go<AK, BKM, false>(p, s);
     }
     static hipError_t launch(int layout, const Params& p, hipStream_t s)
     {
         switch (layout) {
-        case 0: return go<true>(p, s);
-        case 2: return go<false>(p, s);
+        case 0: return go<true, true>(p, s);
+        case 2: return go<false, true>(p, s);
+        case 3: return go<false, false>(p, s);
         default: return DmaInst<TI, TO, BM, BN, BK, WM, WN, MI, 3, 2>::launch(layout, p, s);
         }
     }
