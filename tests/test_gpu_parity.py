@@ -310,8 +310,8 @@ def _config_id(code, name):
 def test_ping_pong_matches_single_group_schedule():
     """The ping-pong config accumulates every C element in the order of the
     3 + 2-stage kernel of the same tile, so the two give identical bits: fp16
-    4096^3 on N(0,1) in all 8 layouts (those with n-contiguous B run that
-    kernel itself), each also checked against the oracle over the whole of
+    4096^3 on N(0,1) in all 8 layouts (A m with B n reads both operands with
+    transposing loads), each also checked against the oracle over the whole of
     C; then ragged bf16 -> bf16 and fp16 -> fp32 shapes (a partial last
     k-tile, 2-tile and 3-tile k ranges, partial edge tiles)."""
     M = N = K = 4096
