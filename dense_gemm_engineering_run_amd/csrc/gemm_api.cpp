@@ -73,6 +73,9 @@ struct Canon {
     bool c_trans;                // C stored transposed (the swap below taken the other way)
 };
 
+// Largest span of one operand's rows, and of its batch entries, in bytes.
+constexpr uint64_t kMaxSpanBytes = (uint64_t)1 << 48;
+
 // Bytes spanned by `outer` rows of `ld` elements whose last row holds
 // `inner` elements rounded up to 16 bytes.
 uint64_t padded_extent(int64_t outer, int64_t inner, int64_t ld, int es)
@@ -124,9 +127,22 @@ int validate(int64_t M, int64_t N, int64_t K, char& a_major, char& b_major, char
     if (lda < std::max<int64_t>(1, a_inner) || ldb < std::max<int64_t>(1, b_inner) ||
         ldc < std::max<int64_t>(1, c_inner))
         return GEMM_ERR_BAD_LD;
-    // Batch strides: non-negative; C entries must not overlap one another.
-    const uint64_t cn = written_extent(c_outer, c_inner, ldc, eo);
     if (sa < 0 || sb < 0 || sc < 0) return GEMM_ERR_BAD_LD;
+    // Upper bounds: the rows of one entry (outer x ld) and the batch entries
+    // (batch x stride) may each span at most 2^48 bytes, the GPU's virtual
+    // address range; every byte offset and extent below then stays far inside
+    // 64 bits.
+    {
+        const uint64_t nb = (uint64_t)std::max<int64_t>(1, batch);
+        auto fits = [&](int64_t outer, int64_t ld, int64_t stride, int e) {
+            const uint64_t lim = kMaxSpanBytes / (uint64_t)e;
+            return (uint64_t)ld <= lim / (uint64_t)std::max<int64_t>(1, outer) && (uint64_t)stride <= lim / nb;
+        };
+        if (!fits(a_outer, lda, sa, es) || !fits(b_outer, ldb, sb, es) || !fits(c_outer, ldc, sc, eo))
+            return GEMM_ERR_BAD_LD;
+    }
+    // C entries must not overlap one another.
+    const uint64_t cn = written_extent(c_outer, c_inner, ldc, eo);
     if (batch > 1 && M > 0 && N > 0 && (uint64_t)sc * eo < cn) return GEMM_ERR_BAD_LD;
 
     const bool reads = M > 0 && N > 0 && K > 0 && batch > 0;

@@ -104,7 +104,9 @@ typedef enum {
     GEMM_ERR_BAD_SHAPE = 2,    /* M, N, K or batch negative, or too large for the tile indexing */
     GEMM_ERR_BAD_MAJOR = 3,    /* major character not in {k,m} / {k,n} / {n,m}          */
     GEMM_ERR_BAD_DTYPE = 4,    /* dtype not a gemm_dtype_t                               */
-    GEMM_ERR_BAD_LD = 5,       /* ld below the contiguous extent (or 1); bad batch stride */
+    GEMM_ERR_BAD_LD = 5,       /* ld below the contiguous extent (or 1); bad batch stride;
+                                  an operand's rows (outer extent x ld) or its batch
+                                  entries (batch x stride) spanning over 2^48 bytes      */
     GEMM_ERR_MISALIGNED = 6,   /* pointer not element-aligned (workspace: 16 bytes), or a
                                   forced config that needs 16-byte alignment the operands lack */
     GEMM_ERR_ALIAS = 7,        /* C's extent overlaps A's or B's                         */

@@ -93,6 +93,17 @@ def test_validation_errors_without_gpu():
     assert run(lda=63) == b.GEMM_ERR_BAD_LD
     assert run(a="m", lda=32) == b.GEMM_ERR_BAD_LD
     assert run(ldc=0, N=0) == b.GEMM_ERR_BAD_LD           # ld must be >= 1
+    # At most 2^48 bytes spanned by an operand's rows: one row of fp32 allows
+    # ld up to 2^46 elements, 64 rows up to 2^40; beyond that (and near 2^63,
+    # where the byte offsets would wrap) the call is refused before any offset
+    # is formed.  At 2^46 validation passes and the launch then refuses the
+    # tile's 32-bit row offsets.
+    assert run(M=1, lda=1 << 46) == b.GEMM_ERR_BAD_SHAPE
+    assert run(M=1, lda=(1 << 46) + 1) == b.GEMM_ERR_BAD_LD
+    assert run(lda=(1 << 40) + 1) == b.GEMM_ERR_BAD_LD
+    assert run(ldb=(1 << 62) + 64) == b.GEMM_ERR_BAD_LD
+    assert run(ldc=(1 << 63) - 1) == b.GEMM_ERR_BAD_LD
+    assert run(a="m", lda=(1 << 61)) == b.GEMM_ERR_BAD_LD
     assert run(A=NULL) == b.GEMM_ERR_NULL_PTR
     assert run(B=NULL) == b.GEMM_ERR_NULL_PTR
     assert run(C=NULL) == b.GEMM_ERR_NULL_PTR
@@ -148,6 +159,11 @@ def test_batched_validation_without_gpu():
     assert run_batched(sa=-64) == b.GEMM_ERR_BAD_LD
     assert run_batched(sc=64 * 64 - 4) == b.GEMM_ERR_BAD_LD     # C entries would overlap
     assert run_batched(sc=0) == b.GEMM_ERR_BAD_LD               # ... also when identical
+    # batch x stride at most 2^48 bytes: two fp32 entries allow strides up to 2^45.
+    assert run_batched(sa=1 << 45, sb=1 << 45, C=1 << 49) == b.GEMM_ERR_HIP
+    assert run_batched(sa=(1 << 45) + 4) == b.GEMM_ERR_BAD_LD
+    assert run_batched(sb=1 << 62) == b.GEMM_ERR_BAD_LD
+    assert run_batched(sc=(1 << 63) - 1) == b.GEMM_ERR_BAD_LD
 
     # A's entries reach into C's range: entry 2 of A starts at 3P.
     assert run_batched(batch=3, sa=(1 << 20) // 4) == b.GEMM_ERR_ALIAS
