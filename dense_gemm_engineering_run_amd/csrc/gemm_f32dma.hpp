@@ -370,6 +370,37 @@ struct F32Dma {
                             }
                         }
                     }
+        } else if constexpr (!BKM && UB::RV > 1 && TO == Out::F32 && !COHERENT && !ROLLED) {
+            // B interleaved (columns RV * c + v of a block in units v = 0 ..
+            // RV-1): for each row a lane holds RV consecutive columns, one
+            // 64- or 128-bit store, whatever A's layout.  Not in the
+            // persistent stream-K kernel's 256x256 tiles (ROLLED): inside its
+            // tile loop this form put the accumulators on the stack (8-13 KB
+            // per lane), so it keeps the element stores below.
+            constexpr int RV = UB::RV;
+            typedef float f32xr __attribute__((ext_vector_type(RV)));
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int cb = 0; cb < UB::NBLK; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int m = rm0 + UA::row(i, (q / 4) * 8 + (lane / 32) * 4 + (q % 4));
+                        const int n = cn0 + cb * UB::BLK + RV * (lane % 32);
+                        f32xr o;
+#pragma unroll
+                        for (int v = 0; v < RV; ++v) o[v] = acc[i][cb * RV + v][q];
+                        float* dst = (float*)p.C + (int64_t)m * p.ldc + n;
+                        if (m < p.M) {
+                            if (VEC && p.c_vec && n + RV - 1 < p.N) {
+                                *(f32xr*)dst = o;
+                            } else {
+#pragma unroll
+                                for (int v = 0; v < RV; ++v)
+                                    if (n + v < p.N) dst[v] = o[v];
+                            }
+                        }
+                    }
         } else if constexpr (COHERENT) {
             // Whole tile, row pitch BN: Units::row is linear in its row
             // argument, so each element's offset is a per-lane part plus a
