@@ -282,11 +282,10 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // 4096, every dtype, operands k-major or m/n-major, one MI355X): large
     // problems (at least a wave of 256x256 tiles) go to the direct-to-LDS
     // 256x256 kernels, mid-size ones to 128x128 direct-to-LDS tiles, small
-    // ones to register-staged 64x64 tiles -- except 16-bit problems with an
-    // m/n-contiguous operand, whose transposing LDS reads make the 128x128
-    // direct-to-LDS tile up to 1.8x faster even there.  A strided batch
-    // counts all its entries' tiles (64 x 512^3 fp16: the 256x256 tile runs
-    // at 507 TF/s, the 64x64 one at 296).
+    // ones to 64x64 tiles (register-staged for fp32, direct-to-LDS for
+    // 16-bit inputs).  A strided batch counts all its entries' tiles
+    // (64 x 512^3 fp16: the 256x256 tile runs at 507 TF/s, the register-staged
+    // 64x64 one at 296).
     const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0) * (double)std::max<int64_t>(batch, 1);
     if (dtype == GEMM_DTYPE_F32) {
         if (tiles256 >= 256) return pick("256x256x32 w2x2 mfma32 s2 dma");
@@ -312,8 +311,16 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // the 32x32x16 form's transposing LDS reads suit it better (up to 30 %).
     if (tiles256 >= 64)
         return pick(a_kmajor && b_kmajor ? "128x128x64 w2x2 mfma16 s4 dma" : "128x128x64 w2x2 mfma32 s4 dma");
-    if (tiles256 >= 16 && !(a_kmajor && b_kmajor)) return pick("128x128x64 w2x2 mfma32 s4 dma");
-    return pick("64x64x64 w2x2 mfma16 s2 swz");
+    // Small: up to one wave of 64x64 tiles (256), the 64x64 direct-to-LDS
+    // tile with a 4-stage ring, on 32x32x16 MFMAs only when neither operand is
+    // k-contiguous (256^2 .. 1024^2, K 512 .. 4096: 5-8 us; 12-35 % ahead of
+    // the 128x128 tile and up to 2.5x ahead of the register-staged 64x64 one
+    // with m/n-contiguous operands); past that the 128x128 tile (1536^2:
+    // 12.3-13.7 us against 14.0-17.2).
+    const double tiles64 = std::ceil(M / 64.0) * std::ceil(N / 64.0) * (double)std::max<int64_t>(batch, 1);
+    if (tiles64 <= 256)
+        return pick(!a_kmajor && !b_kmajor ? "64x64x64 w2x2 mfma32 s4 dma" : "64x64x64 w2x2 mfma16 s4 dma");
+    return pick(a_kmajor && b_kmajor ? "128x128x64 w2x2 mfma16 s4 dma" : "128x128x64 w2x2 mfma32 s4 dma");
 }
 
 // Built-in choice among the element-by-element configs (operands that are
