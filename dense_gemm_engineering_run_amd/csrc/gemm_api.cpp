@@ -287,10 +287,17 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // (64 x 512^3 fp16: the 256x256 tile runs at 507 TF/s, the register-staged
     // 64x64 one at 296).
     const double tiles256 = std::ceil(M / 256.0) * std::ceil(N / 256.0) * (double)std::max<int64_t>(batch, 1);
+    const double tiles64 = std::ceil(M / 64.0) * std::ceil(N / 64.0) * (double)std::max<int64_t>(batch, 1);
     if (dtype == GEMM_DTYPE_F32) {
         if (tiles256 >= 256) return pick("256x256x32 w2x2 mfma32 s2 dma");
         if (tiles256 >= 64) return pick("128x128x32 w2x2 mfma32 s2 dma");
-        return pick("64x64x64 w2x2 mfma16 s2 swz");
+        // Small: the 64x64 direct-to-LDS tile from 256 tiles of 64x64 up
+        // (1024^2 .. 1536^2: 5-15 % ahead of the register-staged 64x64 tile);
+        // below, the register-staged 32x32x128 tile (512^2, 768x512: about
+        // twice as fast as either 64x64 tile, whose few workgroups leave CUs
+        // idle).
+        if (tiles64 > 128) return pick("64x64x32 w2x2 mfma32 s4 dma");
+        return pick("32x32x128 w2x2 mfma16 s2 swz");
     }
     // Large problems with k-contiguous B (or k-contiguous A: the ping-pong
     // config then stores C transposed, with the operands the other way round)
@@ -317,7 +324,6 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // the 128x128 tile and up to 2.5x ahead of the register-staged 64x64 one
     // with m/n-contiguous operands); past that the 128x128 tile (1536^2:
     // 12.3-13.7 us against 14.0-17.2).
-    const double tiles64 = std::ceil(M / 64.0) * std::ceil(N / 64.0) * (double)std::max<int64_t>(batch, 1);
     if (tiles64 <= 256)
         return pick(!a_kmajor && !b_kmajor ? "64x64x64 w2x2 mfma32 s4 dma" : "64x64x64 w2x2 mfma16 s4 dma");
     return pick(a_kmajor && b_kmajor ? "128x128x64 w2x2 mfma16 s4 dma" : "128x128x64 w2x2 mfma32 s4 dma");
