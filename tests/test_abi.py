@@ -550,3 +550,35 @@ def test_log_env_prints_the_choice():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
                        timeout=120)
     assert r.returncode == 0 and "mi355_gemm:" not in r.stderr
+
+
+def test_heuristic_picks_without_table():
+    """With no tuning table the built-in heuristic chooses by C's shorter
+    side first (thin problems take tiles no wider than it), then by tile
+    counts: the register-staged 32x32 fp32 tile and the 64x64 direct tiles
+    for small problems, 128x128 in between, 256x256 (the ping-pong config
+    for 16-bit inputs with a k-contiguous operand and K >= 1024) for large."""
+    cases = [
+        (65536, 64, 1024, "k", "k", "n", 0, "f32 64x64x32 w2x2 mfma32 s4 dma"),
+        (4096, 64, 1024, "k", "k", "n", 0, "f32 32x32x128 w2x2 mfma16 s2 swz"),
+        (512, 512, 512, "k", "k", "n", 0, "f32 32x32x128 w2x2 mfma16 s2 swz"),
+        (1024, 1024, 1024, "m", "n", "n", 0, "f32 64x64x32 w2x2 mfma32 s4 dma"),
+        (2048, 2048, 1024, "k", "n", "n", 0, "f32 128x128x32 w2x2 mfma32 s2 dma"),
+        (32768, 128, 1024, "m", "n", "n", 0, "f32 128x128x32 w2x2 mfma32 s2 dma"),
+        (8192, 8192, 8192, "m", "n", "n", 0, "f32 256x256x32 w2x2 mfma32 s2 dma"),
+        (65536, 64, 4096, "k", "k", "n", 1, "f16_f32 64x64x64 w2x2 mfma16 s4 dma"),
+        (64, 65536, 4096, "m", "n", "m", 1, "f16_f32 64x64x64 w2x2 mfma32 s4 dma"),
+        (65536, 128, 4096, "k", "k", "n", 2, "bf16_bf16 128x128x64 w2x2 mfma16 s4 dma"),
+        (1024, 1024, 1024, "k", "n", "n", 3, "f16_f16 64x64x64 w2x2 mfma16 s4 dma"),
+        (1024, 1024, 4096, "m", "n", "n", 4, "bf16_f32 64x64x64 w2x2 mfma32 s4 dma"),
+        (2048, 2048, 2048, "m", "k", "n", 1, "f16_f32 128x128x64 w2x2 mfma32 s4 dma"),
+        (4096, 4096, 4096, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
+        (8192, 8192, 512, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma32 s2 dma"),
+    ]
+    code = "import dense_gemm_engineering_run_amd as g\ng.gemm_load_tuning(None)\n"
+    for M, N, K, a, bm, c, d, _ in cases:
+        code += f"print(g.gemm_config_describe({d}, g.gemm_select_config({M}, {N}, {K}, '{a}', '{bm}', '{c}', {d})))\n"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    got = r.stdout.strip().splitlines()
+    assert got == [want for *_, want in cases], list(zip(got, [c[:7] for c in cases]))
