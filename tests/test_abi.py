@@ -554,8 +554,8 @@ def test_log_env_prints_the_choice():
 
 def test_heuristic_picks_without_table():
     """With no tuning table the built-in heuristic chooses by C's shorter
-    side first (thin problems take tiles no wider than it), then by tile
-    counts: the register-staged 32x32 fp32 tile and the 64x64 direct tiles
+    side first (thin problems take tiles no wider than it) and, for 16-bit
+    inputs, a K of at most 256 (64x64 tiles), then by tile counts: the register-staged 32x32 fp32 tile and the 64x64 direct tiles
     for small problems, 128x128 in between, 256x256 (the ping-pong config
     for 16-bit inputs with a k-contiguous operand and K >= 1024) for large."""
     cases = [
@@ -569,6 +569,8 @@ def test_heuristic_picks_without_table():
         (65536, 64, 4096, "k", "k", "n", 1, "f16_f32 64x64x64 w2x2 mfma16 s4 dma"),
         (64, 65536, 4096, "m", "n", "m", 1, "f16_f32 64x64x64 w2x2 mfma32 s4 dma"),
         (65536, 128, 4096, "k", "k", "n", 2, "bf16_bf16 128x128x64 w2x2 mfma16 s4 dma"),
+        (16384, 128, 128, "k", "k", "n", 1, "f16_f32 64x64x64 w2x2 mfma16 s4 dma"),
+        (32768, 512, 512, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s2 dma"),
         (1024, 1024, 1024, "k", "n", "n", 3, "f16_f16 64x64x64 w2x2 mfma16 s4 dma"),
         (1024, 1024, 4096, "m", "n", "n", 4, "bf16_f32 64x64x64 w2x2 mfma32 s4 dma"),
         (2048, 2048, 2048, "m", "k", "n", 1, "f16_f32 128x128x64 w2x2 mfma32 s4 dma"),
