@@ -299,11 +299,15 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
             return pick(tiles64 > 128 ? "64x64x32 w2x2 mfma32 s4 dma" : "32x32x128 w2x2 mfma16 s2 swz");
         return pick(!a_kmajor && !b_kmajor ? "64x64x64 w2x2 mfma32 s4 dma" : "64x64x64 w2x2 mfma16 s4 dma");
     }
-    // A short K (at most 256: four k-tiles or fewer per tile) on up to 4096
-    // tiles of 64x64: 16-bit inputs take the 64x64 direct tile (16384 x 128
-    // x 128 and 8192 x 256 x 256: 15-17 % ahead of the 128x128 tile).
-    if (dtype != GEMM_DTYPE_F32 && K <= 256 && tiles64 <= 4096)
+    // A short K (at most 256: a few k-tiles per tile) on up to 1024 tiles of
+    // 64x64: the small-problem tiles below (16384 x 128 x 128: 15-17 % ahead
+    // of the 128x128 tile for 16-bit inputs, 1.5x for fp32; at 4096^2 x 256,
+    // 4096 such tiles, the 256x256 tile is ahead again).
+    if (K <= 256 && tiles64 <= 1024) {
+        if (dtype == GEMM_DTYPE_F32)
+            return pick(tiles64 > 128 ? "64x64x32 w2x2 mfma32 s4 dma" : "32x32x128 w2x2 mfma16 s2 swz");
         return pick(!a_kmajor && !b_kmajor ? "64x64x64 w2x2 mfma32 s4 dma" : "64x64x64 w2x2 mfma16 s4 dma");
+    }
     if (short_side <= 128 && tiles256 >= 64) {
         if (dtype == GEMM_DTYPE_F32) return pick("128x128x32 w2x2 mfma32 s2 dma");
         return pick(a_kmajor && b_kmajor ? "128x128x64 w2x2 mfma16 s4 dma" : "128x128x64 w2x2 mfma32 s4 dma");

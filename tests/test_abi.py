@@ -570,6 +570,8 @@ def test_heuristic_picks_without_table():
         (64, 65536, 4096, "m", "n", "m", 1, "f16_f32 64x64x64 w2x2 mfma32 s4 dma"),
         (65536, 128, 4096, "k", "k", "n", 2, "bf16_bf16 128x128x64 w2x2 mfma16 s4 dma"),
         (16384, 128, 128, "k", "k", "n", 1, "f16_f32 64x64x64 w2x2 mfma16 s4 dma"),
+        (16384, 128, 128, "k", "k", "n", 0, "f32 64x64x32 w2x2 mfma32 s4 dma"),
+        (4096, 4096, 256, "k", "k", "n", 0, "f32 256x256x32 w2x2 mfma32 s2 dma"),
         (32768, 512, 512, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s2 dma"),
         (1024, 1024, 1024, "k", "n", "n", 3, "f16_f16 64x64x64 w2x2 mfma16 s4 dma"),
         (1024, 1024, 4096, "m", "n", "n", 4, "bf16_f32 64x64x64 w2x2 mfma32 s4 dma"),
