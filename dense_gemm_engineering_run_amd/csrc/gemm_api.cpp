@@ -333,7 +333,10 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // of tiles and for 16-bit outputs; with fp32 outputs on grids of several
     // waves (8192^2, 16384^2) the 32x32x16 form stays 3-7 % ahead.
     if (tiles256 >= 192) {
-        if ((a_kmajor || b_kmajor) && K >= 1024) return pick("256x256x64 w4x2 mfma16 s3x2 pp");
+        // With both operands m/n-contiguous the ping-pong kernel reads both
+        // with transposing loads: level with the one-group kernels on one
+        // wave of tiles, 2-10 % ahead from 512 tiles (8192^2) up.
+        if (K >= 1024 && (a_kmajor || b_kmajor || tiles256 >= 512)) return pick("256x256x64 w4x2 mfma16 s3x2 pp");
         return pick(kDtypes[dtype].out_bytes == 4 && tiles256 >= 512 ? "256x256x64 w4x2 mfma32 s2 dma"
                                                                       : "256x256x64 w4x2 mfma16 s2 dma");
     }

@@ -348,9 +348,10 @@ def test_select_config_is_host_logic():
 def test_heuristic_for_large_untuned_16bit_shapes():
     """Shapes far from every tuned key take the heuristic: with K >= 1024 and
     a k-contiguous operand the ping-pong 256x256 config (for A k, B n it
-    stores C transposed with the operands swapped); otherwise the 256x256
-    tile on 16x16x32 MFMAs, except for fp32 outputs on grids of 512 or more
-    of its tiles, which keep the 32x32x16 form."""
+    stores C transposed with the operands swapped), and with neither
+    operand k-contiguous from 512 such tiles up; otherwise the 256x256 tile
+    on 16x16x32 MFMAs, except for fp32 outputs on grids of 512 or more of
+    its tiles, which keep the 32x32x16 form."""
     def chosen(M, N, K, d, a="k", b="k"):
         return g.gemm_config_describe(d, g.gemm_select_config(M, N, K, a, b, "n", d))
     assert chosen(16384, 16384, 1024, 3) == "f16_f16 256x256x64 w4x2 mfma16 s3x2 pp"
@@ -359,9 +360,10 @@ def test_heuristic_for_large_untuned_16bit_shapes():
     assert chosen(16384, 16384, 1024, 1, a="m") == "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"
     assert chosen(16384, 16384, 1024, 3, b="n") == "f16_f16 256x256x64 w4x2 mfma16 s3x2 pp"
     assert chosen(16384, 16384, 512, 3) == "f16_f16 256x256x64 w4x2 mfma16 s2 dma"
-    assert chosen(16384, 16384, 1024, 3, a="m", b="n") == "f16_f16 256x256x64 w4x2 mfma16 s2 dma"
-    assert chosen(3008, 12000, 3008, 2, a="m", b="n") == "bf16_bf16 256x256x64 w4x2 mfma16 s2 dma"
-    assert chosen(16384, 16384, 1024, 1, a="m", b="n") == "f16_f32 256x256x64 w4x2 mfma32 s2 dma"
+    assert chosen(16384, 16384, 1024, 3, a="m", b="n") == "f16_f16 256x256x64 w4x2 mfma16 s3x2 pp"
+    assert chosen(3008, 12000, 3008, 2, a="m", b="n") == "bf16_bf16 256x256x64 w4x2 mfma16 s3x2 pp"
+    assert chosen(16384, 16384, 1024, 1, a="m", b="n") == "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"
+    assert chosen(16384, 16384, 512, 1, a="m", b="n") == "f16_f32 256x256x64 w4x2 mfma32 s2 dma"
     assert chosen(16384, 16384, 512, 4) == "bf16_f32 256x256x64 w4x2 mfma32 s2 dma"
     # mid-size (64 to 191 tiles of 256x256): the 128x128 tile, on 16x16x32
     # MFMAs only when both operands are k-contiguous
@@ -578,6 +580,8 @@ def test_heuristic_picks_without_table():
         (2048, 2048, 2048, "m", "k", "n", 1, "f16_f32 128x128x64 w2x2 mfma32 s4 dma"),
         (4096, 4096, 4096, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
         (8192, 8192, 512, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma32 s2 dma"),
+        (8192, 8192, 4096, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
+        (4096, 4096, 4096, "m", "n", "n", 2, "bf16_bf16 256x256x64 w4x2 mfma16 s2 dma"),
     ]
     code = "import dense_gemm_engineering_run_amd as g\ng.gemm_load_tuning(None)\n"
     for M, N, K, a, bm, c, d, _ in cases:
