@@ -332,7 +332,7 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
     // clock under the power limit than on 32x32x16 ones and wins on one wave
     // of tiles and for 16-bit outputs; with fp32 outputs on grids of several
     // waves (8192^2, 16384^2) the 32x32x16 form stays 3-7 % ahead.
-    if (tiles256 >= 192) {
+    if (tiles256 >= 128) {
         // With both operands m/n-contiguous the ping-pong kernel reads both
         // with transposing loads: level with the one-group kernels on one
         // wave of tiles, 2-10 % ahead from 512 tiles (8192^2) up.
@@ -340,9 +340,15 @@ int heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool a_kmajor, bool b_
         return pick(kDtypes[dtype].out_bytes == 4 && tiles256 >= 512 ? "256x256x64 w4x2 mfma32 s2 dma"
                                                                       : "256x256x64 w4x2 mfma16 s2 dma");
     }
-    // Mid-size: the 128x128 tile, on 16x16x32 MFMAs when both operands are
-    // k-contiguous (5-10 % faster at 2048^2); with an m/n-contiguous operand
-    // the 32x32x16 form's transposing LDS reads suit it better (up to 30 %).
+    // From half a wave of 256x256 tiles up (128; 2560 x 4096 .. 3328^2) the
+    // branch above: those tiles ran 1.3-1.5x ahead of 128x128 ones, whose
+    // four-stage ring fits one workgroup per CU and so takes 2-3 rounds.
+    // Below that, with an operand k-contiguous, the 128x256 tile (one round;
+    // 2304^2 .. 2816^2: 10-16 % ahead of 128x128).  Then the 128x128 tile,
+    // on 16x16x32 MFMAs when both operands are k-contiguous (5-10 % faster
+    // at 2048^2); with an m/n-contiguous operand the 32x32x16 form's
+    // transposing LDS reads suit it better (up to 30 %).
+    if (tiles256 > 64 && (a_kmajor || b_kmajor)) return pick("128x256x64 w2x2 mfma32 s3 dma");
     if (tiles256 >= 64)
         return pick(a_kmajor && b_kmajor ? "128x128x64 w2x2 mfma16 s4 dma" : "128x128x64 w2x2 mfma32 s4 dma");
     // Small: up to one wave of 64x64 tiles (256), the 64x64 direct-to-LDS

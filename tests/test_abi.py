@@ -365,9 +365,9 @@ def test_heuristic_for_large_untuned_16bit_shapes():
     assert chosen(16384, 16384, 1024, 1, a="m", b="n") == "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"
     assert chosen(16384, 16384, 512, 1, a="m", b="n") == "f16_f32 256x256x64 w4x2 mfma32 s2 dma"
     assert chosen(16384, 16384, 512, 4) == "bf16_f32 256x256x64 w4x2 mfma32 s2 dma"
-    # mid-size (64 to 191 tiles of 256x256): the 128x128 tile, on 16x16x32
-    # MFMAs only when both operands are k-contiguous
-    assert chosen(2560, 2560, 16384, 1) == "f16_f32 128x128x64 w2x2 mfma16 s4 dma"
+    # mid-size (65 to 127 tiles of 256x256): the 128x256 tile with a
+    # k-contiguous operand, else the 128x128 tile on 32x32x16 MFMAs
+    assert chosen(2560, 2560, 16384, 1) == "f16_f32 128x256x64 w2x2 mfma32 s3 dma"
     sel = g.gemm_select_config(2560, 2560, 16384, "m", "n", "n", 1)
     assert g.gemm_config_describe(1, sel) == "f16_f32 128x128x64 w2x2 mfma32 s4 dma"
 
@@ -578,6 +578,9 @@ def test_heuristic_picks_without_table():
         (1024, 1024, 1024, "k", "n", "n", 3, "f16_f16 64x64x64 w2x2 mfma16 s4 dma"),
         (1024, 1024, 4096, "m", "n", "n", 4, "bf16_f32 64x64x64 w2x2 mfma32 s4 dma"),
         (2048, 2048, 2048, "m", "k", "n", 1, "f16_f32 128x128x64 w2x2 mfma32 s4 dma"),
+        (2304, 2304, 2048, "k", "k", "n", 1, "f16_f32 128x256x64 w2x2 mfma32 s3 dma"),
+        (3072, 3072, 1024, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
+        (3072, 3072, 2048, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s2 dma"),
         (4096, 4096, 4096, "k", "k", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
         (8192, 8192, 512, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma32 s2 dma"),
         (8192, 8192, 4096, "m", "n", "n", 1, "f16_f32 256x256x64 w4x2 mfma16 s3x2 pp"),
